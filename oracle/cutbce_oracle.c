@@ -1,0 +1,275 @@
+/*
+ * TEST INFRASTRUCTURE -- float64 CPU oracle for the fused full-vocabulary binary cross-entropy.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may build, load or call this file.
+ * It shares no code, header or constant with the GPU library and is deliberately plain and slow: every
+ * logit z is formed as an explicit dot product, in float64, with d ascending, and nothing is blocked,
+ * fused or reordered beyond what the definitions below state.
+ *
+ * What it computes ("Cut Binary Cross Entropy", Li, Ning, Hammad):
+ *   - Section III-A, Eq. (1)-(2): per logit x and target y in {0,1}, the BCE loss in its stable form
+ *       L(x, y) = max(x, 0) + log(1 + exp(-|x|)) - y * x .
+ *   - Section III-A, Eq. (3): per position, the sum over all V items, divided by V; then (Section III-B, the
+ *     paragraph after Eq. (4)) averaged over positions with padding positions left out. Together:
+ *       loss = 1 / (R_v * V) * sum_{valid rows r} sum_{v < V} L(z_rv, y_rv),  z_rv = H[r] . E[v].
+ *   - Section III-B, Eq. (4): dL/dz_rv = s * (sigma(z_rv) - y_rv) with s = 1 / (R_v * V), hence
+ *       dH[r] = g * s * sum_v (sigma(z_rv) - y_rv) E[v]   (valid rows; masked rows get 0),
+ *       dE[v] = g * s * sum_{valid r} (sigma(z_rv) - y_rv) H[r],
+ *     where g is the upstream cotangent of the scalar loss (the custom-VJP input).
+ *
+ * Readings where the paper is silent (each is listed in the design notes):
+ *   - targets are given per row as a list of ids; y_rv = 1 iff v appears in row r's list (a repeated id
+ *     counts once, since y is binary in Section III-A);
+ *   - the per-position `weights` of the paper's API are read as a 0/1 row mask; positives of masked rows
+ *     are ignored;
+ *   - R_v = 0 (every row masked) gives loss 0 and zero gradients;
+ *   - row_loss[r] is the unnormalised sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
+ *
+ * Inputs H and E are read either as IEEE float32 or as bfloat16 (dtype 0 / 1), each element converted
+ * exactly to double before use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_BAD_SHAPE 1
+#define OR_BAD_IDS 2
+#define OR_NOMEM 3
+
+/* Planted mistakes: compiled in only for the tests that prove the pins catch them. */
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+static double load_elem(const void *p, int dtype, size_t i) {
+    if (dtype == 0) return (double)((const float *)p)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t *)p)[i]) << 16; /* bfloat16 = top half of a float32 */
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double dot_rv(const void *H, const void *E, int dtype, int64_t r, int64_t v, int D) {
+    double z = 0.0;
+    for (int d = 0; d < D; ++d) z += load_elem(H, dtype, (size_t)r * D + d) * load_elem(E, dtype, (size_t)v * D + d);
+    return z;
+}
+
+/* Eq. (2): L(x, 0) = max(x, 0) + log(1 + exp(-|x|)). */
+static double softplus(double x) {
+#if ORACLE_PLANT == 5
+    return log1p(exp(-fabs(x))); /* planted: drops max(x, 0) */
+#else
+    return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+#endif
+}
+
+/* sigma(x), evaluated without overflow on either side. */
+static double sigmoid(double x) {
+    if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+    double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* Check CSR consistency and id range; count valid rows. */
+static int check_inputs(int64_t R, int64_t V, int D, const int32_t *row_offsets, const int32_t *item_ids,
+                        const uint8_t *row_mask, int64_t *n_valid) {
+    if (R < 0 || V < 1 || D < 1) return OR_BAD_SHAPE;
+    if (row_offsets[0] != 0) return OR_BAD_IDS;
+    int64_t rv = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        if (row_offsets[r + 1] < row_offsets[r]) return OR_BAD_IDS;
+        for (int64_t p = row_offsets[r]; p < row_offsets[r + 1]; ++p)
+            if (item_ids[p] < 0 || item_ids[p] >= V) return OR_BAD_IDS;
+        if (row_mask[r]) ++rv;
+    }
+    *n_valid = rv;
+    return OR_OK;
+}
+
+/* y_rv for one row: mark the row's ids in a V-sized byte map (repeated ids collapse). */
+static void mark_row(const int32_t *row_offsets, const int32_t *item_ids, int64_t r, uint8_t *ymap, int on) {
+    for (int64_t p = row_offsets[r]; p < row_offsets[r + 1]; ++p) ymap[item_ids[p]] = (uint8_t)on;
+}
+
+static int cmp_i32(const void *a, const void *b) {
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Is v among row r's ids? `sorted_ids` holds each row's ids sorted (same CSR offsets). */
+static int row_has(const int32_t *row_offsets, const int32_t *sorted_ids, int64_t r, int32_t v) {
+    int64_t lo = row_offsets[r], hi = row_offsets[r + 1];
+    while (lo < hi) {
+        int64_t mid = (lo + hi) / 2;
+        if (sorted_ids[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo < row_offsets[r + 1] && sorted_ids[lo] == v;
+}
+
+static int32_t *sorted_copy(int64_t R, const int32_t *row_offsets, const int32_t *item_ids) {
+    int64_t nnz = row_offsets[R];
+    int32_t *s = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+    if (!s) return NULL;
+    if (nnz) memcpy(s, item_ids, sizeof(int32_t) * (size_t)nnz);
+    for (int64_t r = 0; r < R; ++r)
+        qsort(s + row_offsets[r], (size_t)(row_offsets[r + 1] - row_offsets[r]), sizeof(int32_t), cmp_i32);
+    return s;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Row side: for each requested row (n_rows entries of `rows`; all R rows when rows == NULL) compute
+ * row_loss[i] = sum_v L(z, y) (0 for a masked row) and, when dH != NULL, dH[i][:] = g*s*sum_v (sigma-y) E[v]
+ * (0 for a masked row). s uses the global R_v of the full mask.
+ */
+int oracle_rows(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
+                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
+                int64_t n_rows, const int64_t *rows, double *row_loss, double *dH) {
+    int64_t rv;
+    int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
+    if (st) return st;
+    if (!rows) n_rows = R;
+    double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
+#if ORACLE_PLANT == 2
+    s = 1.0 / ((double)R * (double)V); /* planted: padding rows counted in the average */
+#endif
+    int err = 0;
+#pragma omp parallel
+    {
+        uint8_t *ymap = (uint8_t *)calloc((size_t)V, 1);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!ymap || !acc) {
+#pragma omp atomic write
+            err = OR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (!ymap || !acc) continue;
+            int64_t r = rows ? rows[i] : i;
+            if (r < 0 || r >= R) {
+#pragma omp atomic write
+                err = OR_BAD_SHAPE;
+                continue;
+            }
+            if (!row_mask[r]) {
+                row_loss[i] = 0.0;
+                if (dH) for (int d = 0; d < D; ++d) dH[(size_t)i * D + d] = 0.0;
+                continue;
+            }
+            mark_row(row_offsets, item_ids, r, ymap, 1);
+            double lsum = 0.0;
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                double z = dot_rv(H, E, dtype, r, v, D);
+                double y = ymap[v] ? 1.0 : 0.0;
+#if ORACLE_PLANT == 1
+                lsum += softplus(z); /* planted: sparse target correction dropped */
+#else
+                lsum += softplus(z) - y * z;
+#endif
+                if (dH) {
+#if ORACLE_PLANT == 3
+                    double gz = y - sigmoid(z); /* planted: sign of the logit gradient flipped */
+#else
+                    double gz = sigmoid(z) - y;
+#endif
+                    for (int d = 0; d < D; ++d) acc[d] += gz * load_elem(E, dtype, (size_t)v * D + d);
+                }
+            }
+            mark_row(row_offsets, item_ids, r, ymap, 0);
+            row_loss[i] = lsum;
+            if (dH) for (int d = 0; d < D; ++d) dH[(size_t)i * D + d] = g * s * acc[d];
+        }
+        free(ymap);
+        free(acc);
+    }
+    return err;
+}
+
+/* Item side: dE[i][:] = g*s*sum_{valid r} (sigma(z_r,v) - y_r,v) H[r] for each requested item (all V when
+ * items == NULL). */
+int oracle_items(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
+                 const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
+                 int64_t n_items, const int64_t *items, double *dE) {
+    int64_t rv;
+    int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
+    if (st) return st;
+    if (!items) n_items = V;
+    double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
+    int32_t *sorted = sorted_copy(R, row_offsets, item_ids);
+    if (!sorted) return OR_NOMEM;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!acc) {
+#pragma omp atomic write
+            err = OR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < n_items; ++i) {
+            if (!acc) continue;
+            int64_t v = items ? items[i] : i;
+            if (v < 0 || v >= V) {
+#pragma omp atomic write
+                err = OR_BAD_SHAPE;
+                continue;
+            }
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                if (!row_mask[r]) continue;
+                double z = dot_rv(H, E, dtype, r, v, D);
+                double y = row_has(row_offsets, sorted, r, (int32_t)v) ? 1.0 : 0.0;
+                double gz = sigmoid(z) - y;
+#if ORACLE_PLANT == 4
+                /* planted: transposed operand -- uses E[v] where H[r] belongs */
+                for (int d = 0; d < D; ++d) acc[d] += gz * load_elem(E, dtype, (size_t)v * D + d);
+#else
+                for (int d = 0; d < D; ++d) acc[d] += gz * load_elem(H, dtype, (size_t)r * D + d);
+#endif
+            }
+            for (int d = 0; d < D; ++d) dE[(size_t)i * D + d] = g * s * acc[d];
+        }
+        free(acc);
+    }
+    free(sorted);
+    return err;
+}
+
+/* Whole problem: loss = s * sum of valid row losses in ascending row order, plus optional row_loss [R],
+ * dH [R][D] and dE [V][D]. */
+int oracle_full(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
+                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
+                double *loss, double *row_loss, double *dH, double *dE) {
+    int64_t rv;
+    int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
+    if (st) return st;
+    double *rl = row_loss ? row_loss : (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    if (!rl) return OR_NOMEM;
+    st = oracle_rows(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, g, R, NULL, rl, dH);
+    if (!st && dE) st = oracle_items(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, g, V, NULL, dE);
+    if (!st) {
+        double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
+#if ORACLE_PLANT == 2
+        s = 1.0 / ((double)R * (double)V);
+#endif
+        double tot = 0.0;
+        for (int64_t r = 0; r < R; ++r) tot += rl[r];
+        *loss = s * tot;
+    }
+    if (!row_loss) free(rl);
+    return st;
+}

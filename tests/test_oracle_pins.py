@@ -1,0 +1,285 @@
+"""Pins for the float64 oracle: each check ties it to something other than itself.
+
+* Eq. (1) of "Cut Binary Cross Entropy" (Section III-A), evaluated in 50-digit arithmetic with mpmath,
+  against the oracle's stable form on single logits.
+* The identity softplus(z) - softplus(-z) = z and the asymptotes of softplus.
+* Whole-problem closed forms: E = 0 and H = 0 make every logit 0, so the loss is ln 2 and the gradients
+  reduce to the rank-1 background (1/2) plus the sparse target corrections.
+* Fifth-order finite differences of the oracle loss, on inputs where every perturbation is exact.
+* A library special case: PyTorch's binary_cross_entropy_with_logits + autograd in float64 on the dense
+  logits (Eq. (2)-(4) with a materialised multi-hot Y), on tiny inputs.
+* Invariants: masked rows, repeated ids, row/item permutations, linearity in the cotangent g, all rows masked.
+* Planted mistakes: oracle builds with a deliberate error (dropped sparse term, wrong normaliser, flipped
+  gradient sign, transposed operand, dropped max(x,0)) must each fail at least one pin.
+"""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vocabulary_label_bce_amd import workloads as W
+
+mpmath.mp.dps = 50
+
+
+def _single(z, y, plant=0):
+    """Oracle loss for one logit z (R = V = D = 1, so s = 1)."""
+    H = np.array([[z]], np.float32)
+    E = np.array([[1.0]], np.float32)
+    ro = np.array([0, 1 if y else 0], np.int32)
+    ids = np.array([0] if y else [], np.int32)
+    return oracle.full(H, E, ro, ids, np.array([1], np.uint8), plant=plant)["loss"]
+
+
+def _eq1(z, y):
+    x = mpmath.mpf(z)
+    sig = 1 / (1 + mpmath.exp(-x))
+    return float(-y * mpmath.log(sig) - (1 - y) * mpmath.log(1 - sig))
+
+
+ZS = [-30.0, -12.5, -3.25, -1.0, -0.125, -2.0 ** -12, 0.0, 2.0 ** -12, 0.125, 1.0, 3.25, 12.5, 30.0]
+
+
+def pin_elementwise(plant=0):
+    """Worst |oracle - Eq.(1)| in units of the allowed error: 1e-13 relative, plus a few ulps of |z| because
+    the stable form L(z,0) - y*z cancels when y = 1 and z >> 0."""
+    worst = 0.0
+    eps = 2.0 ** -52
+    for z in ZS:
+        for y in (0, 1):
+            ref = _eq1(z, y)
+            got = _single(z, y, plant)
+            worst = max(worst, abs(got - ref) / (1e-13 * abs(ref) + 8 * eps * (1 + abs(z))))
+    return worst
+
+
+def test_elementwise_matches_eq1():
+    assert pin_elementwise() < 1.0
+
+
+def test_softplus_odd_part_and_asymptotes():
+    for z in ZS:
+        assert _single(z, 0) - _single(-z, 0) == pytest.approx(z, rel=1e-14, abs=1e-15)
+    # z -> -inf: L(z, 0) ~ exp(z); z -> +inf: L(z, 0) ~ z + exp(-z); L(z, 1) = L(-z, 0)
+    assert _single(-40.0, 0) == pytest.approx(math.exp(-40.0), rel=1e-12)
+    assert _single(40.0, 0) == pytest.approx(40.0 + math.exp(-40.0), rel=1e-15)
+    assert _single(40.0, 1) == pytest.approx(math.exp(-40.0), rel=1e-12)
+
+
+def _problem(R=9, V=13, D=5, seed=3, mask_frac=0.25, dup_frac=0.3, dtype="f32"):
+    p = W.custom_problem(R, V, D, dtype=dtype, seed=seed, h_std=0.7, e_std=0.9, pos_per_row=(0, 4),
+                         mask_frac=mask_frac, dup_frac=dup_frac)
+    # make sure some masked row carries positives too (they must be ignored)
+    return p
+
+
+def _valid_sets(p):
+    ro = p["row_offsets"].numpy()
+    ids = p["item_ids"].numpy()
+    return [set(ids[ro[r]:ro[r + 1]].tolist()) for r in range(len(ro) - 1)]
+
+
+def pin_zero_E(plant=0, g=1.7):
+    p = _problem()
+    H = p["H"].numpy().astype(np.float64)
+    E0 = np.zeros_like(p["E"].numpy())
+    m = p["row_mask"].numpy()
+    out = oracle.full(p["H"], E0, p["row_offsets"], p["item_ids"], p["row_mask"], g=g, plant=plant)
+    R, V = H.shape[0], E0.shape[0]
+    Rv = int(m.sum())
+    s = 1.0 / (Rv * V)
+    sets = _valid_sets(p)
+    dE_ref = np.zeros((V, H.shape[1]))
+    half = 0.5 * H[m == 1].sum(0)
+    for v in range(V):
+        corr = sum((H[r] for r in range(R) if m[r] and v in sets[r]), np.zeros(H.shape[1]))
+        dE_ref[v] = g * s * (half - corr)
+    err = max(abs(out["loss"] - math.log(2.0)) / math.log(2.0),
+              np.abs(out["dH"]).max(),
+              np.abs(out["dE"] - dE_ref).max() / np.abs(dE_ref).max())
+    return err
+
+
+def pin_zero_H(plant=0, g=-0.6):
+    p = _problem(seed=5)
+    E = p["E"].numpy().astype(np.float64)
+    H0 = np.zeros_like(p["H"].numpy())
+    m = p["row_mask"].numpy()
+    out = oracle.full(H0, p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=g, plant=plant)
+    R, V = H0.shape[0], E.shape[0]
+    s = 1.0 / (int(m.sum()) * V)
+    sets = _valid_sets(p)
+    dH_ref = np.zeros((R, E.shape[1]))
+    for r in range(R):
+        if m[r]:
+            dH_ref[r] = g * s * (0.5 * E.sum(0) - sum((E[v] for v in sets[r]), np.zeros(E.shape[1])))
+    err = max(abs(out["loss"] - math.log(2.0)) / math.log(2.0),
+              np.abs(out["dE"]).max(),
+              np.abs(out["dH"] - dH_ref).max() / np.abs(dH_ref).max())
+    return err
+
+
+def test_zero_E_closed_form():
+    assert pin_zero_E() < 1e-13
+
+
+def test_zero_H_closed_form():
+    assert pin_zero_H() < 1e-13
+
+
+def pin_finite_differences(plant=0):
+    """5-point central differences of the oracle loss vs its dH and dE (g = 1)."""
+    rng = np.random.default_rng(11)
+    R, V, D = 4, 6, 3
+    q = 2.0 ** -10  # every value and every perturbation is a multiple of 2^-10: exact in float32
+    H = (np.round(rng.normal(0, 1.0, (R, D)) / q) * q).astype(np.float32)
+    E = (np.round(rng.normal(0, 1.0, (V, D)) / q) * q).astype(np.float32)
+    ro = np.array([0, 2, 2, 5, 6], np.int32)
+    ids = np.array([1, 4, 0, 5, 0, 3], np.int32)  # row 2 has a repeated id
+    m = np.array([1, 1, 0, 1], np.uint8)
+    out = oracle.full(H, E, ro, ids, m, plant=plant)
+
+    def L(Hx, Ex):
+        return oracle.full(Hx, Ex, ro, ids, m, grads=False, plant=plant)["loss"]
+
+    eps = 8 * q
+    worst = 0.0
+    for which, X, G in (("H", H, out["dH"]), ("E", E, out["dE"])):
+        for idx in np.ndindex(X.shape):
+            vals = []
+            for k in (-2, -1, 1, 2):
+                Y = X.copy()
+                Y[idx] += k * eps
+                vals.append(L(Y, E) if which == "H" else L(H, Y))
+            fd = (vals[0] - 8 * vals[1] + 8 * vals[2] - vals[3]) / (12 * eps)
+            worst = max(worst, abs(fd - G[idx]) / (np.abs(G).max()))
+    return worst
+
+
+def test_finite_differences():
+    assert pin_finite_differences() < 1e-7
+
+
+def pin_torch_dense(plant=0, dtype="f32"):
+    """PyTorch float64 BCE-with-logits + autograd on the materialised logits (tiny sizes only)."""
+    p = _problem(R=11, V=17, D=6, seed=9, dtype=dtype)
+    m = p["row_mask"].numpy().astype(bool)
+    H = p["H"].to(torch.float64).requires_grad_(True)
+    E = p["E"].to(torch.float64).requires_grad_(True)
+    Z = H @ E.T
+    Y = torch.zeros_like(Z)
+    sets = _valid_sets(p)
+    for r, st in enumerate(sets):
+        for v in st:
+            Y[r, v] = 1.0
+    per = torch.nn.functional.binary_cross_entropy_with_logits(Z, Y, reduction="none")
+    mt = torch.from_numpy(m)
+    loss = per[mt].sum() / (mt.sum() * Z.shape[1])
+    loss.backward()
+    out = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], plant=plant)
+    err = max(abs(out["loss"] - loss.item()) / abs(loss.item()),
+              np.abs(out["dH"] - H.grad.numpy()).max() / np.abs(H.grad.numpy()).max(),
+              np.abs(out["dE"] - E.grad.numpy()).max() / np.abs(E.grad.numpy()).max(),
+              np.abs(out["row_loss"][m] - per.sum(1).detach().numpy()[m]).max())
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_torch_dense_special_case(dtype):
+    assert pin_torch_dense(dtype=dtype) < 1e-12
+
+
+def test_masked_rows_have_no_effect():
+    p = _problem(seed=21, mask_frac=0.4)
+    m = p["row_mask"].numpy()
+    assert (m == 0).any()
+    a = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"])
+    H2 = p["H"].clone()
+    H2[torch.from_numpy(m == 0)] = 3.0
+    b = oracle.full(H2, p["E"], p["row_offsets"], p["item_ids"], p["row_mask"])
+    assert a["loss"] == b["loss"]
+    np.testing.assert_array_equal(a["dE"], b["dE"])
+    assert np.all(b["dH"][m == 0] == 0.0) and np.all(b["row_loss"][m == 0] == 0.0)
+
+
+def test_repeated_ids_collapse():
+    p = _problem(seed=4, dup_frac=0.0)
+    ro, ids = p["row_offsets"].numpy(), p["item_ids"].numpy()
+    rows = [np.concatenate([ids[ro[r]:ro[r + 1]], ids[ro[r]:ro[r + 1]][:2]]) for r in range(len(ro) - 1)]
+    ro2 = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
+    ids2 = np.concatenate(rows).astype(np.int32)
+    assert ids2.size > ids.size
+    a = oracle.full(p["H"], p["E"], ro, ids, p["row_mask"])
+    b = oracle.full(p["H"], p["E"], ro2, ids2, p["row_mask"])
+    assert a["loss"] == b["loss"]
+    np.testing.assert_array_equal(a["dH"], b["dH"])
+    np.testing.assert_array_equal(a["dE"], b["dE"])
+
+
+def test_permutation_equivariance():
+    p = _problem(seed=8)
+    R, V = p["H"].shape[0], p["E"].shape[0]
+    rng = np.random.default_rng(0)
+    pr, pv = rng.permutation(R), rng.permutation(V)
+    inv_v = np.argsort(pv)
+    ro, ids = p["row_offsets"].numpy(), p["item_ids"].numpy()
+    rows = [inv_v[ids[ro[r]:ro[r + 1]]] for r in pr]
+    ro2 = np.concatenate([[0], np.cumsum([len(x) for x in rows])]).astype(np.int32)
+    ids2 = np.concatenate(rows).astype(np.int32)
+    a = oracle.full(p["H"], p["E"], ro, ids, p["row_mask"])
+    b = oracle.full(p["H"][pr], p["E"][pv], ro2, ids2, p["row_mask"][pr])
+    assert a["loss"] == pytest.approx(b["loss"], rel=1e-13)
+    np.testing.assert_allclose(a["dH"][pr], b["dH"], rtol=1e-12, atol=1e-17)
+    np.testing.assert_allclose(a["dE"][pv], b["dE"], rtol=1e-12, atol=1e-17)
+
+
+def test_linear_in_cotangent_and_all_masked():
+    p = _problem(seed=12)
+    a = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=1.0)
+    b = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=-2.5)
+    np.testing.assert_allclose(b["dH"], -2.5 * a["dH"], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(b["dE"], -2.5 * a["dE"], rtol=1e-14, atol=0)
+    assert a["loss"] == b["loss"]
+    z = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], torch.zeros_like(p["row_mask"]))
+    assert z["loss"] == 0.0 and not z["dH"].any() and not z["dE"].any()
+
+
+def test_subset_entry_points_agree_with_full():
+    p = _problem(seed=14)
+    a = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.75)
+    rr = [0, 3, 5, 8]
+    b = oracle.rows(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], rr, g=0.75)
+    c = oracle.items(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], [1, 7, 12], g=0.75)
+    np.testing.assert_array_equal(b["row_loss"], a["row_loss"][rr])
+    np.testing.assert_array_equal(b["dH"], a["dH"][rr])
+    np.testing.assert_array_equal(c["dE"], a["dE"][[1, 7, 12]])
+
+
+def test_rejects_bad_ids():
+    H = np.zeros((2, 3), np.float32)
+    E = np.zeros((4, 3), np.float32)
+    with pytest.raises(ValueError):
+        oracle.full(H, E, np.array([0, 1, 2], np.int32), np.array([0, 4], np.int32), np.ones(2, np.uint8))
+    with pytest.raises(ValueError):
+        oracle.full(H, E, np.array([0, 2, 1], np.int32), np.array([0, 1], np.int32), np.ones(2, np.uint8))
+
+
+def test_dense_logits_size_matches_paper():
+    # Section I-A: 16 x 256 x 876,939 float32 logits take about 13.38 GiB.
+    assert W.dense_logits_bytes(16 * 256, 876_939) / 2 ** 30 == pytest.approx(13.38, abs=0.005)
+
+
+PINS = [pin_elementwise, pin_zero_E, pin_zero_H, pin_finite_differences, pin_torch_dense]
+TOL = {pin_elementwise: 1.0, pin_zero_E: 1e-13, pin_zero_H: 1e-13, pin_finite_differences: 1e-7,
+       pin_torch_dense: 1e-12}
+
+
+@pytest.mark.parametrize("plant", [1, 2, 3, 4, 5])
+def test_planted_mistakes_are_caught(plant):
+    """1: sparse term dropped; 2: padding counted in the average; 3: gradient sign flipped;
+    4: E used where H belongs in dE; 5: max(x, 0) dropped from softplus."""
+    caught = [f.__name__ for f in PINS if not f(plant=plant) < TOL[f]]
+    assert caught, f"planted mistake {plant} passed every pin"
