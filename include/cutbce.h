@@ -1,0 +1,115 @@
+/*
+ * cutbce.h -- C ABI of the MI355X (gfx950) fused full-vocabulary binary cross-entropy library (libcutbce.so).
+ *
+ * The operation ("Cut Binary Cross Entropy", Li, Ning, Hammad):
+ *   rows r < R carry hidden states H[r] (D values), items v < V carry embeddings E[v]; the logit is
+ *   z_rv = H[r] . E[v] (Section III-A). Row r's positive items are a list of ids; y_rv = 1 iff v is in the
+ *   list (a repeated id counts once). Rows with row_mask[r] == 0 are padding and take no part.
+ *   With R_v = number of valid rows and s = 1 / (R_v * V):
+ *     loss   = s * sum_{valid r} sum_v [ max(z,0) + log(1 + exp(-|z|)) - y*z ]      (Eq. (2)-(3) and the
+ *                                                                                   averaging after Eq. (4))
+ *     dH[r]  = g * s * sum_v (sigma(z_rv) - y_rv) * E[v]        for valid r, 0 for masked r   (Eq. (4))
+ *     dE[v]  = g * s * sum_{valid r} (sigma(z_rv) - y_rv) * H[r]                             (Eq. (4))
+ *   where g is the cotangent of the scalar loss. R_v = 0 gives loss 0 and zero gradients.
+ *   The logits Z and their gradient are never written to memory (Section III-B, Table I): every kernel forms
+ *   its [rows x items] tile in registers and reduces it on chip.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) must point to device memory of the GPU that is current on the calling thread;
+ *     pointers marked (host) to host memory. The caller owns and allocates all memory; the library never
+ *     allocates device memory and keeps no state between calls.
+ *   - H [R][D], E [V][D], dH [R][D], dE [V][D] are dense row-major, in the problem's element type, 16-byte
+ *     aligned. row_offsets int32 [R+1] (row_offsets[0] = 0, non-decreasing, row_offsets[R] = nnz); item_ids
+ *     int32 [nnz], any order within a row, repeats allowed; row_mask uint8 [R] (0 = padding, else valid).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs asynchronously; no call
+ *     synchronises with the host. Scalars that the device produces or consumes (loss, grad_loss) stay in
+ *     device memory.
+ *   - Host-side argument checks run before anything is enqueued; on any error nothing is enqueued and the
+ *     outputs are untouched. Ids outside [0, V) or inconsistent row_offsets are not checked by the compute
+ *     entry points (they are skipped if encountered); cutbce_validate_targets checks them on the device.
+ *   - Results are deterministic: the same inputs on the same device give bitwise identical outputs (no
+ *     floating-point atomics).
+ *   - The workspace is scratch: its contents on entry are ignored and on return are unspecified. Concurrent
+ *     calls must use distinct workspaces.
+ */
+#ifndef CUTBCE_H
+#define CUTBCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CUTBCE_OK = 0,
+    CUTBCE_ERR_NULL = 1,        /* a required pointer is NULL */
+    CUTBCE_ERR_SHAPE = 2,       /* R < 1, V < 1, nnz < 0, or sizes overflow the supported range */
+    CUTBCE_ERR_DTYPE = 3,       /* unknown element type */
+    CUTBCE_ERR_ALIGN = 4,       /* H, E, dH, dE, workspace not 16-byte aligned, or int arrays not 4-byte */
+    CUTBCE_ERR_WORKSPACE = 5,   /* workspace smaller than cutbce_workspace_size() */
+    CUTBCE_ERR_UNSUPPORTED = 6, /* (dtype, D) combination without a kernel: see cutbce_problem */
+    CUTBCE_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+} cutbce_status;
+
+typedef enum {
+    CUTBCE_F32 = 0, /* IEEE float32 inputs, float32 MFMA, float32 gradients */
+    CUTBCE_BF16 = 1 /* bfloat16 inputs, bf16 MFMA with float32 accumulation, bfloat16 gradients */
+} cutbce_dtype;
+
+/* Problem description (host struct). Supported: bf16 with D in {64, 128, 256, 512}; f32 with D in
+ * {64, 128, 256}. R, V < 2^31 - 256; nnz < 2^31. */
+typedef struct {
+    int64_t rows;  /* R = B*N positions (Section III-A flattens batch and sequence) */
+    int64_t vocab; /* V items */
+    int64_t nnz;   /* length of item_ids */
+    int32_t dim;   /* D */
+    int32_t dtype; /* cutbce_dtype */
+} cutbce_problem;
+
+/* Bytes of device workspace that cutbce_forward and cutbce_backward need for this problem (host call).
+ * Grows with V*D (one re-laid-out copy of E for the forward's gradient GEMM), R*D and nnz; never with R*V. */
+cutbce_status cutbce_workspace_size(const cutbce_problem *p, size_t *bytes);
+
+/* Forward (Section III-A, Eq. (2)-(3); Section III-C's forward sweep over vocabulary blocks).
+ *   loss      (device) float [1]: the scalar loss above.
+ *   row_loss  (device) float [R] or NULL: sum_v [softplus(z_rv) - y_rv z_rv] per valid row (not divided by
+ *             R_v*V), 0 for masked rows.
+ *   dh_saved  (device) float [R][D] or NULL: when given, the same sweep also forms
+ *             s * sum_v (sigma(z_rv) - y_rv) E[v] (the dH of Eq. (4) for g = 1; 0 for masked rows) so that
+ *             cutbce_backward can return dH without recomputing the logits for it.
+ */
+cutbce_status cutbce_forward(const cutbce_problem *p, const void *H, const void *E,
+                             const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                             float *loss, float *row_loss, float *dh_saved,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward (Section III-B, Eq. (4); the custom VJP recomputes logit tiles on chip).
+ *   grad_loss (device) float [1]: the cotangent g.
+ *   dh_saved  (device) float [R][D] or NULL: the forward's dh_saved for these same inputs. When NULL and dH
+ *             is requested, dH is computed here by recomputing the logits.
+ *   dH        (device) [R][D] in the element type, or NULL to skip: overwritten with g * (dH of Eq. (4)).
+ *   dE        (device) [V][D] in the element type, or NULL to skip: overwritten with g * (dE of Eq. (4)).
+ */
+cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void *E,
+                              const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                              const float *grad_loss, const float *dh_saved, void *dH, void *dE,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device-side check of the targets: writes to *bad (device int32) the number of ids outside [0, V) plus
+ * the number of rows whose offsets decrease, plus 1 if row_offsets[0] != 0 or row_offsets[R] != nnz.
+ * 0 means the targets are well formed. Needs no workspace. */
+cutbce_status cutbce_validate_targets(const cutbce_problem *p, const int32_t *row_offsets,
+                                      const int32_t *item_ids, int32_t *bad, void *stream);
+
+/* Static description of a status code (host). */
+const char *cutbce_status_string(cutbce_status s);
+
+/* Library version as major*10000 + minor*100 + patch (host). */
+int cutbce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CUTBCE_H */

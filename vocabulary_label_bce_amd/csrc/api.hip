@@ -1,0 +1,201 @@
+// C ABI of libcutbce.so (declared in include/cutbce.h): argument checks, workspace layout, and the sequence of
+// launches for the forward and backward of the fused full-vocabulary BCE.
+#include <string.h>
+
+#include "../../include/cutbce.h"
+#include "common.h"
+
+using namespace cutbce;
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool supported(int dtype, int D) {
+  if (dtype == CUTBCE_BF16) return D == 64 || D == 128 || D == 256 || D == 512;
+  if (dtype == CUTBCE_F32) return D == 64 || D == 128 || D == 256;
+  return false;
+}
+
+cutbce_status check_problem(const cutbce_problem* p) {
+  if (!p) return CUTBCE_ERR_NULL;
+  if (p->dtype != CUTBCE_F32 && p->dtype != CUTBCE_BF16) return CUTBCE_ERR_DTYPE;
+  if (p->rows < 1 || p->vocab < 1 || p->nnz < 0 || p->dim < 1) return CUTBCE_ERR_SHAPE;
+  if (p->rows > (int64_t)0x7fffffff - 1024 || p->vocab > (int64_t)0x7fffffff - 1024 || p->nnz > 0x7fffffffLL)
+    return CUTBCE_ERR_SHAPE;
+  if (!supported(p->dtype, p->dim)) return CUTBCE_ERR_UNSUPPORTED;
+  return CUTBCE_OK;
+}
+
+Layout make_layout(const cutbce_problem* p) {
+  Layout L;
+  memset(&L, 0, sizeof L);
+  L.R = p->rows;
+  L.V = p->vocab;
+  L.nnz = p->nnz;
+  L.D = p->dim;
+  L.dtype = p->dtype;
+  L.esz = p->dtype == CUTBCE_BF16 ? 2 : 4;
+  L.R_pad = round_up(L.R, kPad);
+  L.V_pad = round_up(L.V, kPad);
+  const int nw = sweep_waves(L.dtype, L.D);
+  L.rows_per_wg = nw * 32;
+  L.items_per_wg = nw * 32;
+  L.n_rt = L.R_pad / L.rows_per_wg;
+  L.n_vt = L.V_pad / L.items_per_wg;
+  L.n_rs = L.R_pad / 32;
+  L.n_vs = L.V_pad / 32;
+  L.n_eblk = (L.V_pad + kEBlkItems - 1) / kEBlkItems;
+  L.nb_r = L.n_rt * L.n_vs;
+  L.nb_i = L.n_vt * L.n_rs;
+  // forward-sweep partials are indexed by unit: at most max(1024 units, every row tile once) x rows_per_wg
+  const int64_t part_rows = (L.n_rt > 1024 ? L.n_rt : 1024) * (int64_t)L.rows_per_wg;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.off_ctl = take(256);
+  L.off_row_of = take(sizeof(int32_t) * L.R_pad);
+  L.off_compact_of = take(sizeof(int32_t) * L.R);
+  L.off_rptr = take(sizeof(int32_t) * 2 * L.R_pad);
+  L.off_Hc = take((size_t)L.R_pad * L.D * L.esz);
+  L.off_Hrp = take((size_t)L.R_pad * L.D * L.esz);
+  L.off_sumH = take(sizeof(double) * L.D);
+  L.off_sumH_part = take(sizeof(double) * L.D * (L.R_pad / 32));
+  L.off_sumE = take(sizeof(double) * L.D);
+  L.off_sumE_part = take(sizeof(double) * L.D * L.n_eblk);
+  L.off_Evp = take((size_t)L.V_pad * L.D * L.esz);
+  L.off_dhpart = take(sizeof(float) * (size_t)part_rows * L.D);
+  L.off_rowpart = take(sizeof(float) * 2 * (size_t)part_rows);
+  L.off_rowloss = take(sizeof(double) * L.R_pad);
+  L.off_dhtmp = take(sizeof(float) * (size_t)L.R * L.D);
+  L.off_bptr_r = take(sizeof(int32_t) * (L.nb_r + 1));
+  L.off_bfill_r = take(sizeof(int32_t) * L.nb_r);
+  L.off_pairs_r = take(sizeof(int32_t) * 2 * (L.nnz > 0 ? L.nnz : 1));
+  L.off_bptr_i = take(sizeof(int32_t) * (L.nb_i + 1));
+  L.off_bfill_i = take(sizeof(int32_t) * L.nb_i);
+  L.off_pairs_i = take(sizeof(int32_t) * 2 * (L.nnz > 0 ? L.nnz : 1));
+  const int64_t nbmax = L.nb_r > L.nb_i ? L.nb_r : L.nb_i;
+  L.scan_elems = (size_t)((nbmax + 1 + kScanBlock - 1) / kScanBlock + 1);
+  L.off_scan = take(sizeof(int32_t) * L.scan_elems);
+  L.total = o;
+  return L;
+}
+
+bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) != 0; }
+
+cutbce_status hip_status(hipError_t e) { return e == hipSuccess ? CUTBCE_OK : CUTBCE_ERR_HIP; }
+
+#define TRY(x)                                 \
+  do {                                         \
+    hipError_t e_ = (x);                       \
+    if (e_ != hipSuccess) return CUTBCE_ERR_HIP; \
+  } while (0)
+
+cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E, const int32_t* ro,
+                           const int32_t* ids, const uint8_t* mask, void* ws, size_t ws_bytes, Layout* L) {
+  cutbce_status s = check_problem(p);
+  if (s != CUTBCE_OK) return s;
+  if (!H || !E || !ro || !mask || !ws || (p->nnz > 0 && !ids)) return CUTBCE_ERR_NULL;
+  if (misaligned(H, 16) || misaligned(E, 16) || misaligned(ws, 256) || misaligned(ro, 4) || misaligned(ids, 4))
+    return CUTBCE_ERR_ALIGN;
+  *L = make_layout(p);
+  if (ws_bytes < L->total) return CUTBCE_ERR_WORKSPACE;
+  return CUTBCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cutbce_version(void) { return 100; }
+
+const char* cutbce_status_string(cutbce_status s) {
+  switch (s) {
+    case CUTBCE_OK: return "ok";
+    case CUTBCE_ERR_NULL: return "a required pointer is NULL";
+    case CUTBCE_ERR_SHAPE: return "invalid sizes";
+    case CUTBCE_ERR_DTYPE: return "unknown element type";
+    case CUTBCE_ERR_ALIGN: return "misaligned pointer";
+    case CUTBCE_ERR_WORKSPACE: return "workspace too small";
+    case CUTBCE_ERR_UNSUPPORTED: return "unsupported (dtype, dim)";
+    case CUTBCE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+cutbce_status cutbce_workspace_size(const cutbce_problem* p, size_t* bytes) {
+  cutbce_status s = check_problem(p);
+  if (s != CUTBCE_OK) return s;
+  if (!bytes) return CUTBCE_ERR_NULL;
+  *bytes = make_layout(p).total;
+  return CUTBCE_OK;
+}
+
+cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
+                             const int32_t* item_ids, const uint8_t* row_mask, float* loss, float* row_loss,
+                             float* dh_saved, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
+  if (s != CUTBCE_OK) return s;
+  if (!loss) return CUTBCE_ERR_NULL;
+  if (misaligned(dh_saved, 16) || misaligned(loss, 4) || misaligned(row_loss, 4)) return CUTBCE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool with_dh = dh_saved != nullptr;
+  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_prep_h(L, ws, H, false, st));
+  TRY(launch_prep_e(L, ws, E, with_dh, st));
+  TRY(launch_buckets(L, ws, item_ids, true, st));
+  TRY(launch_rows_sweep(L, ws, E, with_dh, st));
+  TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, st));
+  return CUTBCE_OK;
+}
+
+cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
+                              const int32_t* item_ids, const uint8_t* row_mask, const float* grad_loss,
+                              const float* dh_saved, void* dH, void* dE, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Layout L;
+  cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
+  if (s != CUTBCE_OK) return s;
+  if (!grad_loss) return CUTBCE_ERR_NULL;
+  if (misaligned(dh_saved, 16) || misaligned(dH, 16) || misaligned(dE, 16) || misaligned(grad_loss, 4))
+    return CUTBCE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (!dH && !dE) return CUTBCE_OK;
+  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_prep_h(L, ws, H, dE != nullptr, st));
+  if (dE) {
+    TRY(launch_buckets(L, ws, item_ids, false, st));
+    TRY(launch_items_sweep(L, ws, E, grad_loss, dE, st));
+  }
+  if (dH) {
+    if (dh_saved) {
+      TRY(launch_scale_dh(L, dh_saved, grad_loss, dH, st));
+    } else {
+      float* tmp = (float*)(ws + L.off_dhtmp);
+      TRY(launch_prep_e(L, ws, E, true, st));
+      TRY(launch_buckets(L, ws, item_ids, true, st));
+      TRY(launch_rows_sweep(L, ws, E, true, st));
+      TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, st));
+      TRY(launch_scale_dh(L, tmp, grad_loss, dH, st));
+    }
+  }
+  return CUTBCE_OK;
+}
+
+cutbce_status cutbce_validate_targets(const cutbce_problem* p, const int32_t* row_offsets, const int32_t* item_ids,
+                                      int32_t* bad, void* stream) {
+  cutbce_status s = check_problem(p);
+  if (s != CUTBCE_OK) return s;
+  if (!row_offsets || !bad || (p->nnz > 0 && !item_ids)) return CUTBCE_ERR_NULL;
+  if (misaligned(row_offsets, 4) || misaligned(item_ids, 4) || misaligned(bad, 4)) return CUTBCE_ERR_ALIGN;
+  return hip_status(launch_validate(p->rows, p->vocab, p->nnz, row_offsets, item_ids, bad, (hipStream_t)stream));
+}
+
+}  // extern "C"

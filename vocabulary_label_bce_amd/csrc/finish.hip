@@ -1,0 +1,126 @@
+// Finishing kernels: deterministic cross-workgroup reductions of the forward sweep's per-split partials into
+// the loss, the per-row losses and dH, and the cotangent scaling of dH in the backward.
+//
+// Per valid row r the forward sweep leaves, for every vocabulary split, (e, p): e = sum over the split's items
+// of softplus(z) - ln 2 - z/2 and p = sum of z over the row's positives in the split. With the row's logit sum
+// sum_v z_rv = H[r] . (sum_v E[v]) (a rank-1 identity, evaluated in float64), the unnormalised row loss of
+// "Cut Binary Cross Entropy" Eq. (2)-(3) is
+//   V ln 2 + (1/2) H[r].sum_v E[v] + sum_splits e - sum_splits p,
+// and dH[r] = s * (sum_splits dH_part + (1/2) sum_v E[v]) (Eq. (4) with sigma split as (sigma - 1/2) + 1/2).
+#include "common.h"
+
+namespace cutbce {
+
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+__device__ inline double wave_sum(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl, const T* __restrict__ H,
+                                                     const uint8_t* __restrict__ mask,
+                                                     const int32_t* __restrict__ compact_of,
+                                                     const float* __restrict__ dhpart,
+                                                     const float2* __restrict__ rowpart,
+                                                     const double* __restrict__ sumE, int64_t R, int64_t V, int D,
+                                                     int RW, float* __restrict__ row_loss,
+                                                     double* __restrict__ rowloss_c, float* __restrict__ dh_out) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = lane_id();
+  if (r >= R) return;
+  if (mask[r] == 0) {
+    if (row_loss && lane == 0) row_loss[r] = 0.f;
+    if (dh_out)
+      for (int d = lane; d < D; d += 64) dh_out[r * D + d] = 0.f;
+    return;
+  }
+  const int k = compact_of[r];
+  const int S = ctl->splits;
+  const int Tt = (ctl->n_valid + RW - 1) / RW;
+  const int t = k / RW, loc = k % RW;
+  const double scale = ctl->scale;
+  if (dh_out) {
+    for (int d = lane; d < D; d += 64) {
+      double acc = 0.0;
+      for (int s = 0; s < S; ++s) acc += (double)dhpart[((int64_t)(s * Tt + t) * RW + loc) * D + d];
+      dh_out[r * D + d] = (float)(scale * (acc + 0.5 * sumE[d]));
+    }
+  }
+  double e = 0.0, p = 0.0;
+  for (int s = lane; s < S; s += 64) {
+    const float2 q = rowpart[(int64_t)(s * Tt + t) * RW + loc];
+    e += q.x;
+    p += q.y;
+  }
+  double zs = 0.0;
+  for (int d = lane; d < D; d += 64) zs += (double)(float)H[r * D + d] * sumE[d];
+  e = wave_sum(e);
+  p = wave_sum(p);
+  zs = wave_sum(zs);
+  const double rl = (double)V * 0.69314718055994530942 + 0.5 * zs + e - p;
+  if (lane == 0) {
+    if (row_loss) row_loss[r] = (float)rl;
+    rowloss_c[k] = rl;
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_loss_final(const Ctl* __restrict__ ctl, const double* __restrict__ rl,
+                                                     float* __restrict__ loss) {
+  __shared__ double sh[16];
+  const int n = ctl->n_valid;
+  double s = 0.0;
+  for (int k = threadIdx.x; k < n; k += 1024) s += rl[k];
+  s = wave_sum(s);
+  if (lane_id() == 0) sh[threadIdx.x / 64] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < 16; ++w) tot += sh[w];
+    loss[0] = (float)(ctl->scale * tot);
+  }
+}
+
+hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
+                              float* row_loss, float* dh_out, bool with_dh, hipStream_t st) {
+  const unsigned blocks = (unsigned)((L.R + 3) / 4);
+  const Ctl* ctl = (const Ctl*)(ws + L.off_ctl);
+  if (L.dtype == 1) {
+    hipLaunchKernelGGL(k_rows_finish<__bf16>, dim3(blocks), dim3(256), 0, st, ctl, (const __bf16*)H, mask,
+                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
+                       (const float2*)(ws + L.off_rowpart), (const double*)(ws + L.off_sumE), L.R, L.V, L.D,
+                       L.rows_per_wg, row_loss, (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr);
+  } else {
+    hipLaunchKernelGGL(k_rows_finish<float>, dim3(blocks), dim3(256), 0, st, ctl, (const float*)H, mask,
+                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
+                       (const float2*)(ws + L.off_rowpart), (const double*)(ws + L.off_sumE), L.R, L.V, L.D,
+                       L.rows_per_wg, row_loss, (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !loss) return e;
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(1024), 0, st, ctl, (const double*)(ws + L.off_rowloss), loss);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void k_scale_dh(const float* __restrict__ src, const float* __restrict__ g, T* __restrict__ dst,
+                           int64_t n) {
+  const float gg = g[0];
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = (T)(gg * src[i]);
+}
+
+hipError_t launch_scale_dh(const Layout& L, const float* src, const float* grad_loss, void* dH, hipStream_t st) {
+  const int64_t n = L.R * L.D;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (L.dtype == 1)
+    hipLaunchKernelGGL(k_scale_dh<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st, src, grad_loss, (__bf16*)dH, n);
+  else
+    hipLaunchKernelGGL(k_scale_dh<float>, dim3((unsigned)blocks), dim3(256), 0, st, src, grad_loss, (float*)dH, n);
+  return hipGetLastError();
+}
+
+}  // namespace cutbce

@@ -1,0 +1,397 @@
+// Preparation kernels of the CutBCE sweeps (all HBM-bound, small next to the sweeps):
+//   * row compaction: the list of valid rows and R_v from the row mask (padding positions are excluded from
+//     the average, "Cut Binary Cross Entropy" Section III-B after Eq. (4)), with no host synchronisation;
+//   * H preparation: valid rows gathered into a dense, zero-padded Hc, their slot-packed copy Hrp (second
+//     GEMM operand of the dE sweep) and the column sum of the valid rows;
+//   * E preparation: the slot-packed copy Evp (second GEMM operand of the forward/dH sweep) and sum_v E[v];
+//   * positive-id buckets: the sparse targets (Listing 1 keeps them as ids, never as a multi-hot Y) grouped
+//     by the (tile, step) of each sweep, so a wave finds the positives of its current 32x32 logit tile with
+//     two loads;
+//   * a multi-block exclusive scan and the target validation kernel.
+#include "common.h"
+
+namespace cutbce {
+
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+template <typename T> __device__ inline T ld(const T* p) { return *p; }
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+static hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Row compaction: one workgroup walks the mask in chunks of 1024 rows, keeping ascending order.
+// ---------------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask,
+                                                  const int32_t* __restrict__ row_offsets, int64_t R,
+                                                  int64_t R_pad, int64_t V, Ctl* ctl, int32_t* row_of,
+                                                  int32_t* compact_of, int2* rptr) {
+  __shared__ int wsum[16];
+  __shared__ int base_s;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+  if (tid == 0) base_s = 0;
+  __syncthreads();
+  for (int64_t c0 = 0; c0 < R; c0 += 1024) {
+    const int64_t r = c0 + tid;
+    const bool f = r < R && mask[r] != 0;
+    const uint64_t b = __ballot(f);
+    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+    if (lane == 0) wsum[wave] = __popcll(b);
+    __syncthreads();
+    int off = base_s, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) off += wsum[w];
+      tot += wsum[w];
+    }
+    if (r < R) {
+      if (f) {
+        const int k = off + pre;
+        row_of[k] = (int32_t)r;
+        compact_of[r] = k;
+        rptr[k] = make_int2(row_offsets[r], row_offsets[r + 1]);
+      } else {
+        compact_of[r] = -1;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) base_s += tot;
+    __syncthreads();
+  }
+  const int nv = base_s;
+  for (int64_t k = nv + tid; k < R_pad; k += 1024) {
+    row_of[k] = -1;
+    rptr[k] = make_int2(0, 0);
+  }
+  if (tid == 0) {
+    ctl->n_valid = nv;
+    ctl->splits = 0;
+    ctl->bad_ids = 0;
+    ctl->scale = nv > 0 ? 1.0 / ((double)nv * (double)V) : 0.0;
+  }
+}
+
+hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const int32_t* row_offsets,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, row_offsets, L.R, L.R_pad, L.V,
+                     (Ctl*)(ws + L.off_ctl), (int32_t*)(ws + L.off_row_of), (int32_t*)(ws + L.off_compact_of),
+                     (int2*)(ws + L.off_rptr));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// H preparation: block = 32 compacted rows. Hc[k] = H[row_of[k]] (0 for padding), Hrp = slot-packed Hc
+// blocks, per-block column sums (float64) of the valid rows.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const int32_t* __restrict__ row_of,
+                                                int D, T* __restrict__ Hc, T* __restrict__ Hrp,
+                                                double* __restrict__ sum_part) {
+  extern __shared__ char smem_raw[];
+  T* tile = (T*)smem_raw;  // [32][D]
+  const int tid = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * 32;
+  // gather rows (16-byte units)
+  const int upr = D * (int)sizeof(T) / 16;  // 16-byte units per row
+  for (int u = tid; u < 32 * upr; u += 256) {
+    const int rr = u / upr, c = u % upr;
+    const int32_t src = row_of[k0 + rr];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (src >= 0) v = *(const u32x4*)((const char*)H + ((int64_t)src * D) * sizeof(T) + c * 16);
+    *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = v;
+    *(u32x4*)((char*)Hc + ((k0 + rr) * D) * sizeof(T) + c * 16) = v;
+  }
+  __syncthreads();
+  if (Hrp) {
+    T* dst = Hrp + k0 * D;
+    const int runs = (D / 32) * Elem<T>::kGroups * 64;
+    for (int q = tid; q < runs; q += 256) {
+      const int lane = q % 64, g = (q / 64) % Elem<T>::kGroups, db = q / (64 * Elem<T>::kGroups);
+      const int64_t o = slot_off<T>(D, db, g, lane);
+#pragma unroll
+      for (int j = 0; j < Elem<T>::kEPL; ++j)
+        dst[o + j] = tile[acc_pos(g * Elem<T>::kEPL + j, lane / 32) * D + db * 32 + lane % 32];
+    }
+  }
+  for (int d = tid; d < D; d += 256) {
+    double s = 0.0;
+    for (int rr = 0; rr < 32; ++rr) s += (double)(float)tile[rr * D + d];
+    sum_part[blockIdx.x * (int64_t)D + d] = s;
+  }
+}
+
+// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order.
+__global__ void k_sum_parts(const double* __restrict__ part, int64_t nparts, int D, double* __restrict__ out) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= D) return;
+  double s = 0.0;
+  for (int64_t p = 0; p < nparts; ++p) s += part[p * D + d];
+  out[d] = s;
+}
+
+hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st) {
+  const int64_t nblk = L.R_pad / 32;
+  const size_t sm = (size_t)32 * L.D * L.esz;
+  if (L.dtype == 1) {
+    hipLaunchKernelGGL(k_prep_h<__bf16>, dim3((unsigned)nblk), dim3(256), sm, st, (const __bf16*)H,
+                       (const int32_t*)(ws + L.off_row_of), L.D, (__bf16*)(ws + L.off_Hc),
+                       want_hrp ? (__bf16*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
+  } else {
+    hipLaunchKernelGGL(k_prep_h<float>, dim3((unsigned)nblk), dim3(256), sm, st, (const float*)H,
+                       (const int32_t*)(ws + L.off_row_of), L.D, (float*)(ws + L.off_Hc),
+                       want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 255) / 256), dim3(256), 0, st,
+                     (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// E preparation: block = kEBlkItems items, processed 32 at a time through LDS. Writes the slot-packed Evp
+// (when requested) and float64 column sums per block.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t V, int D,
+                                                T* __restrict__ Evp, double* __restrict__ sum_part) {
+  extern __shared__ char smem_raw[];
+  T* tile = (T*)smem_raw;  // [32][D]
+  const int tid = threadIdx.x;
+  const int upr = D * (int)sizeof(T) / 16;
+  double acc0 = 0.0, acc1 = 0.0;  // column sums for d = tid and d = tid + 256
+  const int64_t v_begin = (int64_t)blockIdx.x * kEBlkItems;
+  for (int ch = 0; ch < kEBlkItems / 32; ++ch) {
+    const int64_t v0 = v_begin + ch * 32;
+    for (int u = tid; u < 32 * upr; u += 256) {
+      const int rr = u / upr, c = u % upr;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (v0 + rr < V) x = *(const u32x4*)((const char*)E + ((v0 + rr) * D) * sizeof(T) + c * 16);
+      *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = x;
+    }
+    __syncthreads();
+    if (Evp) {
+      T* dst = Evp + v0 * D;
+      const int runs = (D / 32) * Elem<T>::kGroups * 64;
+      for (int q = tid; q < runs; q += 256) {
+        const int lane = q % 64, g = (q / 64) % Elem<T>::kGroups, db = q / (64 * Elem<T>::kGroups);
+        const int64_t o = slot_off<T>(D, db, g, lane);
+        T tmp[Elem<T>::kEPL];
+#pragma unroll
+        for (int j = 0; j < Elem<T>::kEPL; ++j)
+          tmp[j] = tile[acc_pos(g * Elem<T>::kEPL + j, lane / 32) * D + db * 32 + lane % 32];
+#pragma unroll
+        for (int j = 0; j < Elem<T>::kEPL; ++j) dst[o + j] = tmp[j];
+      }
+    }
+    if (tid < D)
+      for (int rr = 0; rr < 32; ++rr) acc0 += (double)(float)tile[rr * D + tid];
+    if (tid + 256 < D)
+      for (int rr = 0; rr < 32; ++rr) acc1 += (double)(float)tile[rr * D + tid + 256];
+    __syncthreads();
+  }
+  if (tid < D) sum_part[blockIdx.x * (int64_t)D + tid] = acc0;
+  if (tid + 256 < D) sum_part[blockIdx.x * (int64_t)D + tid + 256] = acc1;
+}
+
+hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {
+  const size_t sm = (size_t)32 * L.D * L.esz;
+  if (L.dtype == 1) {
+    hipLaunchKernelGGL(k_prep_e<__bf16>, dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const __bf16*)E, L.V,
+                       L.D, want_evp ? (__bf16*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+  } else {
+    hipLaunchKernelGGL(k_prep_e<float>, dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const float*)E, L.V, L.D,
+                       want_evp ? (float*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 255) / 256), dim3(256), 0, st,
+                     (const double*)(ws + L.off_sumE_part), L.n_eblk, L.D, (double*)(ws + L.off_sumE));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Multi-block exclusive scan of int32 counts, in place: x[i] <- sum_{j<i} x[j] for i <= n (x[n] = total).
+// ---------------------------------------------------------------------------------------------------------
+__device__ inline int block_excl_scan(int v, int* sh, int& total) {
+  // 1024 threads: wave inclusive scan with shuffles, then wave totals through LDS
+  const int lane = lane_id(), wave = threadIdx.x / 64;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) off += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  total = tot;
+  return off + x - v;
+}
+
+constexpr int kScanPerThread = kScanBlock / 1024;
+
+__global__ void __launch_bounds__(1024) k_scan_sums(const int32_t* __restrict__ x, int64_t n,
+                                                    int32_t* __restrict__ bsum) {
+  __shared__ int sh[16];
+  const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPerThread;
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j)
+    if (b0 + j < n) s += x[b0 + j];
+  int tot;
+  block_excl_scan(s, sh, tot);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+}
+
+__global__ void __launch_bounds__(1024) k_scan_bsums(int32_t* bsum, int64_t nb) {
+  __shared__ int sh[16];
+  __shared__ int base;
+  if (threadIdx.x == 0) base = 0;
+  __syncthreads();
+  for (int64_t c0 = 0; c0 < nb; c0 += 1024) {
+    const int64_t i = c0 + threadIdx.x;
+    const int v = i < nb ? bsum[i] : 0;
+    int tot;
+    const int ex = block_excl_scan(v, sh, tot);
+    if (i < nb) bsum[i] = base + ex;
+    __syncthreads();
+    if (threadIdx.x == 0) base += tot;
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_scan_apply(int32_t* __restrict__ x, int64_t n,
+                                                     const int32_t* __restrict__ bsum) {
+  __shared__ int sh[16];
+  const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPerThread;
+  int v[kScanPerThread];
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j) {
+    v[j] = (b0 + j < n) ? x[b0 + j] : 0;
+    s += v[j];
+  }
+  int tot;
+  int run = block_excl_scan(s, sh, tot) + bsum[blockIdx.x];
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j) {
+    if (b0 + j <= n) x[b0 + j] = run;  // entry n receives the grand total
+    run += v[j];
+  }
+}
+
+static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, hipStream_t st) {
+  // n + 1 entries are written; blocks cover [0, n] inclusive
+  const int64_t nb = (n + 1 + kScanBlock - 1) / kScanBlock;
+  hipLaunchKernelGGL(k_scan_sums, dim3((unsigned)nb), dim3(1024), 0, st, x, n, tmp);
+  hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(1024), 0, st, tmp, nb);
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(1024), 0, st, x, n, tmp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Positive-id buckets. One wave per compacted row; pairs (compact row k, item v) go to
+//   rows side : bucket (k / rows_per_wg) * n_vs + v / 32      (forward sweep: row tile x item step)
+//   items side: bucket (v / items_per_wg) * n_rs + k / 32     (backward sweep: item tile x row step)
+// Ids outside [0, V) are skipped and counted. Order inside a bucket is irrelevant: the sweeps OR the
+// positives into a per-lane bit mask, which also makes a repeated id count once.
+// ---------------------------------------------------------------------------------------------------------
+template <bool kScatter>
+__global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
+                                                const int32_t* __restrict__ ids, int64_t V, bool rows_side,
+                                                int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
+                                                int2* __restrict__ pairs, int* bad) {
+  const int64_t k = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = lane_id();
+  if (k >= ctl->n_valid) return;
+  const int2 rp = rptr[k];
+  int nbad = 0;
+  for (int p = rp.x + lane; p < rp.y; p += 64) {
+    const int v = ids[p];
+    if (v < 0 || v >= V) {
+      ++nbad;
+      continue;
+    }
+    const int64_t b = rows_side ? (k / tile) * nsteps_minor + v / 32 : (v / tile) * nsteps_minor + k / 32;
+    if (kScatter) {
+      const int pos = atomicAdd(&cnt[b], 1);
+      pairs[pos] = make_int2((int)k, v);
+    } else {
+      atomicAdd(&cnt[b], 1);
+    }
+  }
+  if (!kScatter && nbad) atomicAdd(bad, nbad);
+}
+
+hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st) {
+  const int64_t nb = rows_side ? L.nb_r : L.nb_i;
+  int32_t* bptr = (int32_t*)(ws + (rows_side ? L.off_bptr_r : L.off_bptr_i));
+  int32_t* bfill = (int32_t*)(ws + (rows_side ? L.off_bfill_r : L.off_bfill_i));
+  int2* pairs = (int2*)(ws + (rows_side ? L.off_pairs_r : L.off_pairs_i));
+  Ctl* ctl = (Ctl*)(ws + L.off_ctl);
+  const int tile = rows_side ? L.rows_per_wg : L.items_per_wg;
+  const int64_t minor = rows_side ? L.n_vs : L.n_rs;
+  hipError_t e = fill_i32(bptr, nb + 1, 0, st);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = L.R_pad / 4;
+  if (L.nnz > 0) {
+    hipLaunchKernelGGL(k_bucket<false>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
+                       (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bptr,
+                       (int2*)nullptr, &ctl->bad_ids);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = scan_exclusive(bptr, nb, (int32_t*)(ws + L.off_scan), st)) != hipSuccess) return e;
+  if (L.nnz > 0) {
+    if ((e = hipMemcpyAsync(bfill, bptr, nb * sizeof(int32_t), hipMemcpyDeviceToDevice, st)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
+                       (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bfill, pairs,
+                       (int*)nullptr);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Target validation.
+// ---------------------------------------------------------------------------------------------------------
+__global__ void k_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* __restrict__ ro,
+                           const int32_t* __restrict__ ids, int32_t* bad) {
+  int nb = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  for (int64_t r = t0; r < R; r += stride)
+    if (ro[r + 1] < ro[r]) ++nb;
+  for (int64_t p = t0; p < nnz; p += stride)
+    if (ids[p] < 0 || ids[p] >= V) ++nb;
+  if (t0 == 0 && (ro[0] != 0 || ro[R] != nnz)) ++nb;
+  if (nb) atomicAdd(bad, nb);
+}
+
+hipError_t launch_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* row_offsets,
+                           const int32_t* item_ids, int32_t* bad, hipStream_t st) {
+  hipError_t e = fill_i32(bad, 1, 0, st);
+  if (e != hipSuccess) return e;
+  int64_t n = R > nnz ? R : nnz;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_validate, dim3((unsigned)blocks), dim3(256), 0, st, R, V, nnz, row_offsets, item_ids, bad);
+  return hipGetLastError();
+}
+
+}  // namespace cutbce
