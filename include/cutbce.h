@@ -17,7 +17,8 @@
  * Conventions for every entry point:
  *   - Pointers marked (device) must point to device memory of the GPU that is current on the calling thread;
  *     pointers marked (host) to host memory. The caller owns and allocates all memory; the library never
- *     allocates device memory and keeps no state between calls.
+ *     allocates device memory and keeps no state between calls (apart from the opt-in timing records of
+ *     cutbce_profile_enable).
  *   - H [R][D], E [V][D], dH [R][D], dE [V][D] are dense row-major, in the problem's element type, 16-byte
  *     aligned. row_offsets int32 [R+1] (row_offsets[0] = 0, non-decreasing, row_offsets[R] = nnz); item_ids
  *     int32 [nnz], any order within a row, repeats allowed; row_mask uint8 [R] (0 = padding, else valid).
@@ -102,6 +103,15 @@ cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void
  * 0 means the targets are well formed. Needs no workspace. */
 cutbce_status cutbce_validate_targets(const cutbce_problem *p, const int32_t *row_offsets,
                                       const int32_t *item_ids, int32_t *bad, void *stream);
+
+/* Opt-in kernel timing for benchmarks (host calls). While enabled, every launch of the two logit-tile sweeps
+ * (kind 0: forward rows sweep, kind 1: backward dE sweep) is bracketed by HIP events recorded on the launch
+ * stream. cutbce_profile_read waits for those events and returns, per kind, the summed milliseconds and the
+ * number of launches since the last enable/read, then clears them. This is the only state the library keeps
+ * across calls; it is off by default. Enabling (on != 0) clears previous records; at most 65536 launches are
+ * recorded (later ones are not timed). Not thread-safe. */
+cutbce_status cutbce_profile_enable(int on);
+cutbce_status cutbce_profile_read(double *ms, int64_t *launches, int n_kinds);
 
 /* Static description of a status code (host). */
 const char *cutbce_status_string(cutbce_status s);

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function that
+include/cutbce.h declares, sizes its workspace without any [rows, V] term, and rejects bad arguments before
+anything is enqueued (these paths make no HIP call, so fake device pointers are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocabulary_label_bce_amd import binding as B
+from vocabulary_label_bce_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cutbce.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(cutbce_[a-z_]+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = _declared()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in cutbce.h but not exported"
+    assert set(B.EXPORTS) == set(names)
+    assert lib.cutbce_version() >= 100
+
+
+def test_status_strings():
+    lib = B.lib()
+    for code in range(8):
+        assert lib.cutbce_status_string(code)
+    assert lib.cutbce_status_string(0) == b"ok"
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_workspace_has_no_rows_times_vocab_term(name):
+    cfg = W.CONFIGS[name]
+    p = B.problem(cfg.R, cfg.V, 40 * cfg.R, cfg.D, B.BF16 if cfg.dtype == "bf16" else B.F32)
+    ws = B.workspace_size(p)
+    # one re-laid-out copy of E plus O((R + V/256) * D) bookkeeping, never R*V
+    esz = 2 if cfg.dtype == "bf16" else 4
+    assert ws < cfg.V * cfg.D * esz * 1.2 + 1100 * 256 * cfg.D * 4 * 1.5 + 64 * cfg.R * cfg.D + (1 << 26)
+    assert ws < 0.5 * W.dense_logits_bytes(cfg.R, cfg.V) or cfg.R * cfg.V < 1e7
+
+
+def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_bytes=None):
+    lib = B.lib()
+    if ws_bytes is None:
+        try:
+            ws_bytes = B.workspace_size(p)
+        except B.CutBCEError:
+            ws_bytes = 1 << 40
+    vp = ctypes.c_void_p
+    return lib.cutbce_forward(ctypes.byref(p), vp(H), vp(E), vp(ro), vp(ids), vp(mask), vp(loss), None, None,
+                              vp(ws), ws_bytes, None)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every case below fails a host check first
+
+
+def test_forward_rejects_bad_arguments():
+    good = B.problem(64, 4096, 100, 64, B.BF16)
+    assert _call_forward(good, H=0, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 1  # NULL
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=0, ws=FAKE) == 1
+    assert _call_forward(good, H=FAKE + 2, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 4  # align
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE,
+                         ws_bytes=1024) == 5  # workspace
+    bad_dim = B.problem(64, 4096, 100, 96, B.BF16)
+    assert _call_forward(bad_dim, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 6
+    bad_f32 = B.problem(64, 4096, 100, 512, B.F32)
+    assert _call_forward(bad_f32, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 6
+    bad_shape = B.Problem(0, 4096, 100, 64, 1)
+    assert _call_forward(bad_shape, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 2
+    bad_dtype = B.Problem(64, 4096, 100, 64, 7)
+    assert _call_forward(bad_dtype, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 3
+    neg_nnz = B.Problem(64, 4096, -1, 64, 1)
+    assert _call_forward(neg_nnz, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 2
+    # nnz > 0 needs item_ids
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=0, mask=FAKE, loss=FAKE, ws=FAKE) == 1
+
+
+def test_backward_and_validate_reject_bad_arguments():
+    lib = B.lib()
+    p = B.problem(64, 4096, 100, 128, B.BF16)
+    vp = ctypes.c_void_p
+    ws = B.workspace_size(p)
+    # grad_loss NULL
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None,
+                               vp(FAKE), vp(FAKE), vp(FAKE), ws, None) == 1
+    # misaligned dE
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
+                               vp(FAKE), vp(FAKE + 4), vp(FAKE), ws, None) == 4
+    # workspace too small
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
+                               vp(FAKE), vp(FAKE), vp(FAKE), ws - 1, None) == 5
+    assert lib.cutbce_validate_targets(ctypes.byref(p), None, vp(FAKE), vp(FAKE), None) == 1
+    assert lib.cutbce_validate_targets(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE + 2), None) == 4
+    n = ctypes.c_size_t(0)
+    assert lib.cutbce_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.cutbce_workspace_size(ctypes.byref(p), None) == 1
+
+
+def test_library_source_never_allocates_device_memory():
+    csrc = os.path.join(ROOT, "vocabulary_label_bce_amd", "csrc")
+    for f in os.listdir(csrc):
+        txt = open(os.path.join(csrc, f)).read()
+        assert "hipMalloc" not in txt and "hipFree(" not in txt, f

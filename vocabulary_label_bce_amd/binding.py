@@ -31,7 +31,7 @@ class Problem(ctypes.Structure):
 
 
 EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
-           "cutbce_status_string", "cutbce_version"]
+           "cutbce_profile_enable", "cutbce_profile_read", "cutbce_status_string", "cutbce_version"]
 
 
 def lib():
@@ -49,6 +49,10 @@ def lib():
         L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
+        L.cutbce_profile_enable.argtypes = [i32]
+        L.cutbce_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
+        L.cutbce_profile_enable.restype = i32
+        L.cutbce_profile_read.restype = i32
         L.cutbce_status_string.argtypes = [i32]
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
@@ -111,3 +115,20 @@ def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_sa
 def validate_targets(p: Problem, row_offsets, item_ids, bad, stream=None):
     _check(lib().cutbce_validate_targets(ctypes.byref(p), _ptr(row_offsets), _ptr(item_ids), _ptr(bad),
                                          _stream(stream)))
+
+
+SWEEP_KINDS = ("rows_sweep", "items_sweep")
+
+
+def profile_enable(on: bool = True):
+    """Start (or stop) event timing of the two sweep kernels inside the library."""
+    _check(lib().cutbce_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kind: (total_ms, launches)} since the last enable/read; waits for the recorded events."""
+    n = len(SWEEP_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().cutbce_profile_read(ms, cnt, n))
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(SWEEP_KINDS)}

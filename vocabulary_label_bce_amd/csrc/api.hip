@@ -2,6 +2,8 @@
 // launches for the forward and backward of the fused full-vocabulary BCE.
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/cutbce.h"
 #include "common.h"
 
@@ -89,6 +91,52 @@ bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) 
 
 cutbce_status hip_status(hipError_t e) { return e == hipSuccess ? CUTBCE_OK : CUTBCE_ERR_HIP; }
 
+// Opt-in sweep timing (see cutbce_profile_enable).
+struct ProfRec {
+  hipEvent_t a, b;
+  int kind;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pool;
+size_t g_prof_used = 0;
+constexpr size_t kProfMax = 65536;
+
+ProfRec* prof_begin(int kind, hipStream_t st) {
+  if (!g_prof_on || g_prof_used >= kProfMax) return nullptr;
+  if (g_prof_used == g_prof_pool.size()) {
+    ProfRec r;
+    if (hipEventCreate(&r.a) != hipSuccess) return nullptr;
+    if (hipEventCreate(&r.b) != hipSuccess) {
+      (void)hipEventDestroy(r.a);
+      return nullptr;
+    }
+    g_prof_pool.push_back(r);
+  }
+  ProfRec* r = &g_prof_pool[g_prof_used];
+  if (hipEventRecord(r->a, st) != hipSuccess) return nullptr;
+  r->kind = kind;
+  ++g_prof_used;
+  return r;
+}
+
+void prof_end(ProfRec* r, hipStream_t st) {
+  if (r && hipEventRecord(r->b, st) != hipSuccess) r->kind = -1;
+}
+
+hipError_t timed_rows(const Layout& L, char* ws, const void* E, bool with_dh, hipStream_t st) {
+  ProfRec* r = prof_begin(0, st);
+  hipError_t e = launch_rows_sweep(L, ws, E, with_dh, st);
+  prof_end(r, st);
+  return e;
+}
+
+hipError_t timed_items(const Layout& L, char* ws, const void* E, const float* g, void* dE, hipStream_t st) {
+  ProfRec* r = prof_begin(1, st);
+  hipError_t e = launch_items_sweep(L, ws, E, g, dE, st);
+  prof_end(r, st);
+  return e;
+}
+
 #define TRY(x)                                 \
   do {                                         \
     hipError_t e_ = (x);                       \
@@ -150,7 +198,7 @@ cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void*
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_prep_e(L, ws, E, with_dh, st));
   TRY(launch_buckets(L, ws, item_ids, true, st));
-  TRY(launch_rows_sweep(L, ws, E, with_dh, st));
+  TRY(timed_rows(L, ws, E, with_dh, st));
   TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, st));
   return CUTBCE_OK;
 }
@@ -172,7 +220,7 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
   TRY(launch_prep_h(L, ws, H, dE != nullptr, st));
   if (dE) {
     TRY(launch_buckets(L, ws, item_ids, false, st));
-    TRY(launch_items_sweep(L, ws, E, grad_loss, dE, st));
+    TRY(timed_items(L, ws, E, grad_loss, dE, st));
   }
   if (dH) {
     if (dh_saved) {
@@ -181,7 +229,7 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
       float* tmp = (float*)(ws + L.off_dhtmp);
       TRY(launch_prep_e(L, ws, E, true, st));
       TRY(launch_buckets(L, ws, item_ids, true, st));
-      TRY(launch_rows_sweep(L, ws, E, true, st));
+      TRY(timed_rows(L, ws, E, true, st));
       TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, st));
       TRY(launch_scale_dh(L, tmp, grad_loss, dH, st));
     }
@@ -196,6 +244,34 @@ cutbce_status cutbce_validate_targets(const cutbce_problem* p, const int32_t* ro
   if (!row_offsets || !bad || (p->nnz > 0 && !item_ids)) return CUTBCE_ERR_NULL;
   if (misaligned(row_offsets, 4) || misaligned(item_ids, 4) || misaligned(bad, 4)) return CUTBCE_ERR_ALIGN;
   return hip_status(launch_validate(p->rows, p->vocab, p->nnz, row_offsets, item_ids, bad, (hipStream_t)stream));
+}
+
+cutbce_status cutbce_profile_enable(int on) {
+  g_prof_on = on != 0;
+  g_prof_used = 0;
+  return CUTBCE_OK;
+}
+
+cutbce_status cutbce_profile_read(double* ms, int64_t* launches, int n_kinds) {
+  if (!ms || !launches || n_kinds < 0) return CUTBCE_ERR_NULL;
+  for (int k = 0; k < n_kinds; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  cutbce_status st = CUTBCE_OK;
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    ProfRec& r = g_prof_pool[i];
+    if (r.kind < 0 || r.kind >= n_kinds) continue;
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      st = CUTBCE_ERR_HIP;
+      continue;
+    }
+    ms[r.kind] += t;
+    launches[r.kind] += 1;
+  }
+  g_prof_used = 0;
+  return st;
 }
 
 }  // extern "C"

@@ -120,7 +120,13 @@ struct Stager {
   using G = StageGeom<T, D>;
   static constexpr int kUnitsPart = G::kPartBytes / 16;
   static constexpr int kPer = (kUnitsPart + NT - 1) / NT;
+  static constexpr int kSteps = G::kSI / 32;
   u32x4 a[kPer], b[kPer];
+  int bp[kSteps + 1];  // bucket pointers of the stage's steps (bucket range of step j: [bp[j], bp[j+1]))
+  __device__ inline void load_buckets(const int32_t* __restrict__ bptr, int64_t b0) {
+#pragma unroll
+    for (int j = 0; j <= kSteps; ++j) bp[j] = bptr[b0 + j];
+  }
   __device__ inline void load(const T* __restrict__ X, const T* __restrict__ Xsp, int64_t row0, int64_t n_src,
                               int tid) {
 #pragma unroll
@@ -223,25 +229,35 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     float e_acc = 0.f, posz = 0.f;
 
     Stager<T, D, NT, WITH_DH> pf;
+    constexpr int NSS = G::kSI / 32;
+    const int64_t bbase = (int64_t)t * a.n_vs;
     __syncthreads();  // previous unit finished reading LDS
     pf.load(E, Evp, (int64_t)st0 * G::kSI, a.V, tid);
+    pf.load_buckets(a.bptr, bbase + (int64_t)st0 * NSS);
     pf.store(lds, tid);
     __syncthreads();
 
     for (int st = st0; st < st1; ++st) {
       const char* buf = lds + ((st - st0) & 1) * G::kStageBytes;
       const bool more = st + 1 < st1;
-      if (more) pf.load(E, Evp, (int64_t)(st + 1) * G::kSI, a.V, tid);
+      int bcur[NSS + 1];
 #pragma unroll
-      for (int ss = 0; ss < G::kSI / 32; ++ss) {
+      for (int j = 0; j <= NSS; ++j) bcur[j] = __builtin_amdgcn_readfirstlane(pf.bp[j]);
+      if (more) {
+        pf.load(E, Evp, (int64_t)(st + 1) * G::kSI, a.V, tid);
+        pf.load_buckets(a.bptr, bbase + (int64_t)(st + 1) * NSS);
+      }
+#pragma unroll
+      for (int ss = 0; ss < NSS; ++ss) {
         const int v0 = st * G::kSI + ss * 32;
+        typename EL::Op aop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane);
         f32x16 z = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) z = EL::mma(lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane), hop[ks], z);
+        for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], hop[ks], z);
 
-        const int64_t b = (int64_t)t * a.n_vs + v0 / 32;
-        const int pb = __builtin_amdgcn_readfirstlane(a.bptr[b]);
-        const int pe = __builtin_amdgcn_readfirstlane(a.bptr[b + 1]);
+        const int pb = bcur[ss], pe = bcur[ss + 1];
         uint32_t pm = 0u;
         if (pe > pb) pm = positive_mask(a.pairs, pb, pe, r_base, v0, true, lmask, lane);
 
@@ -269,10 +285,15 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
         if (WITH_DH) {
           GPack<T> gp;
           gp.set(c);
+          typename EL::Op bop[NDB][EL::kGroups];
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(buf, ss, db, g, lane), acc[db]);
+            for (int g = 0; g < EL::kGroups; ++g) bop[db][g] = lds_b<T, D>(buf, ss, db, g, lane);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), bop[db][g], acc[db]);
         }
       }
       if (more) pf.store(lds + ((st + 1 - st0) & 1) * G::kStageBytes, tid);
@@ -341,25 +362,35 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   const int n_valid = a.ctl->n_valid;
   const int n_st = (n_valid + G::kSI - 1) / G::kSI;
   Stager<T, D, NT, true> pf;
+  constexpr int NSS = G::kSI / 32;
+  const int64_t bbase = (int64_t)t * a.n_rs;
   if (n_st > 0) {
     pf.load(Hc, Hrp, 0, (int64_t)n_valid, tid);
+    pf.load_buckets(a.bptr, bbase);
     pf.store(lds, tid);
   }
   __syncthreads();
   for (int st = 0; st < n_st; ++st) {
     const char* buf = lds + (st & 1) * G::kStageBytes;
     const bool more = st + 1 < n_st;
-    if (more) pf.load(Hc, Hrp, (int64_t)(st + 1) * G::kSI, (int64_t)n_valid, tid);
+    int bcur[NSS + 1];
 #pragma unroll
-    for (int ss = 0; ss < G::kSI / 32; ++ss) {
+    for (int j = 0; j <= NSS; ++j) bcur[j] = __builtin_amdgcn_readfirstlane(pf.bp[j]);
+    if (more) {
+      pf.load(Hc, Hrp, (int64_t)(st + 1) * G::kSI, (int64_t)n_valid, tid);
+      pf.load_buckets(a.bptr, bbase + (int64_t)(st + 1) * NSS);
+    }
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss) {
       const int r0 = st * G::kSI + ss * 32;
+      typename EL::Op aop[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane);
       f32x16 z = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) z = EL::mma(lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane), eop[ks], z);
+      for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], eop[ks], z);
 
-      const int64_t b = (int64_t)t * a.n_rs + r0 / 32;
-      const int pb = __builtin_amdgcn_readfirstlane(a.bptr[b]);
-      const int pe = __builtin_amdgcn_readfirstlane(a.bptr[b + 1]);
+      const int pb = bcur[ss], pe = bcur[ss + 1];
       uint32_t pm = 0u;
       if (pe > pb) pm = positive_mask(a.pairs, pb, pe, (int)v_own0, r0, false, lmask, lane);
 
@@ -376,10 +407,15 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
       }
       GPack<T> gp;
       gp.set(c);
+      typename EL::Op bop[NDB][EL::kGroups];
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(buf, ss, db, g, lane), acc[db]);
+        for (int g = 0; g < EL::kGroups; ++g) bop[db][g] = lds_b<T, D>(buf, ss, db, g, lane);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), bop[db][g], acc[db]);
     }
     if (more) pf.store(lds + ((st + 1) & 1) * G::kStageBytes, tid);
     __syncthreads();
