@@ -12,12 +12,23 @@
 // The constant 1/2 taken out of sigma is added back as a rank-1 term (1/2 sum_v E[v] for dH, 1/2 sum_r H[r]
 // for dE) in float64 by the finishing kernels: centring keeps the bf16 rounding of G relative to sigma - 1/2,
 // which is what carries the gradient signal when logits are small.
+//
+// Both sweeps share one software-pipelined step engine. Iteration i of a wave issues the MFMAs of the logit
+// tile of step i+1 and of the gradient GEMM of step i-1, while the VALU evaluates the epilogue of step i; the
+// three are independent, so the matrix cores and the vector ALU work at the same time. Streamed operands
+// reach LDS by direct buffer loads (global -> LDS, no registers) into two rings, one for the d-packed operand
+// of the logit GEMM and one for the slot-packed operand of the gradient GEMM, with one workgroup barrier per
+// step.
 #include "common.h"
 
 namespace cutbce {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+#ifndef CUTBCE_SCHED_HINT
+#define CUTBCE_SCHED_HINT 0
+#endif
+constexpr bool kUseHint = CUTBCE_SCHED_HINT != 0;
 
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
@@ -25,10 +36,13 @@ template <typename T> __device__ inline typename Elem<T>::Op load_op(const T* p)
 template <> __device__ inline bf16x8 load_op<__bf16>(const __bf16* p) { return *(const bf16x8*)p; }
 template <> __device__ inline float load_op<float>(const float* p) { return *p; }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // XOR swizzle of 16-byte chunks inside an LDS row of the d-packed operand: lanes reading the same logical
 // chunk of 32 consecutive rows hit distinct banks.
 template <int CPR> __device__ __host__ constexpr inline int swz(int row) {
-  return CPR >= 16 ? (row & 15) : ((row / (16 / CPR)) % CPR);
+  constexpr int rows_per_group = CPR >= 16 ? 1 : 16 / CPR;
+  return CPR >= 16 ? (row & 15) : ((row / rows_per_group) % CPR);
 }
 
 // Pack the 16 accumulator-tile values of a lane into the MFMA operands of the second GEMM.
@@ -41,6 +55,10 @@ template <> struct GPack<__bf16> {
 #pragma unroll
       for (int j = 0; j < 8; ++j) g[q][j] = (__bf16)c[q * 8 + j];
   }
+  __device__ inline void zero() {
+    g[0] = bf16x8{};
+    g[1] = bf16x8{};
+  }
   __device__ inline bf16x8 op(int q) const { return g[q]; }
 };
 template <> struct GPack<float> {
@@ -48,6 +66,10 @@ template <> struct GPack<float> {
   __device__ inline void set(const float* c) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) g[i] = c[i];
+  }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) g[i] = 0.f;
   }
   __device__ inline float op(int q) const { return g[q]; }
 };
@@ -81,11 +103,13 @@ __device__ inline uint32_t positive_mask(const int2* __restrict__ pairs, int pb,
 
 // Choose the number of vocabulary splits S for T row tiles on P persistent workgroups (P a multiple of 8):
 // the unit list (s-major) is cut into 8 contiguous per-XCD ranges; efficiency = U / (P * rounds).
-__device__ inline int choose_splits(int T, int n_stages, int P, int max_units) {
+constexpr int kMaxUnits = 1024;
+__device__ inline int choose_splits(int T, int n_steps, int P) {
   int best_s = 1;
   float best = -1.f;
-  int smax = n_stages < kMaxSplits ? n_stages : kMaxSplits;
-  int cap = max_units / T;
+  int smax = n_steps / 8 < kMaxSplits ? n_steps / 8 : kMaxSplits;  // at least 8 steps per unit
+  if (smax < 1) smax = 1;
+  int cap = kMaxUnits / T;
   if (cap < 1) cap = 1;
   if (smax > cap) smax = cap;
   for (int S = 1; S <= smax; ++S) {
@@ -102,75 +126,277 @@ __device__ inline int choose_splits(int T, int n_stages, int P, int max_units) {
   return best_s;
 }
 
-constexpr int kMaxUnits = 1024;
-
-template <typename T, int D>
-struct StageGeom {
+// ---------------------------------------------------------------------------------------------------------
+// Geometry of the step engine for (T, D, NW waves, GRAD = gradient GEMM present).
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D, int NW, bool GRAD>
+struct Geo {
   static constexpr int kEsz = sizeof(T);
-  static constexpr int kSI = (D * kEsz <= 256) ? 64 : 32;  // streamed rows/items per stage
-  static constexpr int kCPR = D * kEsz / 16;                // 16-byte chunks per d-packed row
-  static constexpr int kPartBytes = kSI * D * kEsz;         // bytes of one stage part
-  static constexpr int kStageBytes = 2 * kPartBytes;        // d-packed part + slot-packed part
+  static constexpr int kStepBytes = 32 * D * kEsz;               // one 32-row block of an operand
+  static constexpr int kRing = kStepBytes <= 16384 ? 3 : 2;      // depth of each operand ring
+  static constexpr int kNA = kRing, kNB = GRAD ? kRing : 0;
+  static constexpr int kCPR = D * kEsz / 16;                     // 16-byte chunks per d-packed row
+  static constexpr int kLoadB = (kStepBytes / NW >= 1024) ? 16 : 4;  // bytes per lane per DMA load
+  static constexpr int kWaveBytes = 64 * kLoadB;                 // bytes one wave instruction moves
+  static constexpr int kLoadsPerPart = kStepBytes / kWaveBytes / NW;
+  static constexpr int kLoadsPerIter = kLoadsPerPart * (GRAD ? 2 : 1) + 1;  // + the bucket-pointer load
+  // loads that may stay in flight at the top of an iteration: a 3-deep ring lets the previous iteration's
+  // loads land one iteration later; a 2-deep ring needs them now
+  static constexpr int kInFlight = kRing >= 3 ? kLoadsPerIter : 0;
+  static constexpr int kLdsBytes = (kNA + kNB) * kStepBytes + NW * 256;
+  static_assert(kLoadsPerPart >= 1 && kStepBytes % (kWaveBytes * NW) == 0, "load split");
+  static_assert(kLoadsPerIter <= 63, "vmcnt range");
 };
 
-// Load one stage (kSI streamed rows of a d-packed matrix X [n][D] and the matching slot-packed blocks of Xsp)
-// into registers: `units` 16-byte pieces per thread. Rows >= n_valid_src read as zero.
-template <typename T, int D, int NT, bool SP>
-struct Stager {
-  using G = StageGeom<T, D>;
-  static constexpr int kUnitsPart = G::kPartBytes / 16;
-  static constexpr int kPer = (kUnitsPart + NT - 1) / NT;
-  static constexpr int kSteps = G::kSI / 32;
-  u32x4 a[kPer], b[kPer];
-  int bp[kSteps + 1];  // bucket pointers of the stage's steps (bucket range of step j: [bp[j], bp[j+1]))
-  __device__ inline void load_buckets(const int32_t* __restrict__ bptr, int64_t b0) {
-#pragma unroll
-    for (int j = 0; j <= kSteps; ++j) bp[j] = bptr[b0 + j];
-  }
-  __device__ inline void load(const T* __restrict__ X, const T* __restrict__ Xsp, int64_t row0, int64_t n_src,
-                              int tid) {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int u = tid + q * NT;
-      if (u < kUnitsPart) {
-        const int r = u / G::kCPR, c = u % G::kCPR;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row0 + r < n_src) x = *(const u32x4*)((const char*)X + (row0 + r) * (int64_t)(D * G::kEsz) + c * 16);
-        a[q] = x;
-        if (SP) b[q] = *(const u32x4*)((const char*)Xsp + row0 * (int64_t)(D * G::kEsz) + (int64_t)u * 16);
-      }
-    }
-  }
-  __device__ inline void store(char* lds, int tid) const {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int u = tid + q * NT;
-      if (u < kUnitsPart) {
-        const int r = u / G::kCPR, c = u % G::kCPR;
-        *(u32x4*)(lds + r * (D * G::kEsz) + ((c ^ swz<G::kCPR>(r)) * 16)) = a[q];
-        if (SP) *(u32x4*)(lds + G::kPartBytes + u * 16) = b[q];
-      }
-    }
-  }
-};
+// Ring barrier. vmcnt(N): this wave's DMA loads older than the last N have landed in LDS. lgkmcnt(0): this
+// wave's own LDS reads have returned -- the compiler may sink the MFMAs that consume them (and their waits)
+// past this asm statement, and a read still queued at the LDS must not see a slot another wave refills
+// after the barrier.
+template <int N> __device__ inline void wait_vm_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
-// A operand of the first GEMM from the d-packed LDS part: streamed row `r` (0..kSI-1), k-step ks.
+// A operand of the logit GEMM from a d-packed LDS block: streamed row `r` (0..31), k-step ks.
 template <typename T, int D>
-__device__ inline typename Elem<T>::Op lds_a(const char* lds, int r, int ks, int lane) {
-  using G = StageGeom<T, D>;
+__device__ inline typename Elem<T>::Op lds_a(const char* blk, int r, int ks, int lane) {
+  constexpr int esz = sizeof(T), cpr = D * esz / 16;
   const int k = ks * Elem<T>::kK + (lane / 32) * Elem<T>::kEPL;  // first feature of this lane
-  const int byte = k * G::kEsz;
+  const int byte = k * esz;
   const int c = byte / 16, w = byte % 16;
-  return load_op<T>((const T*)(lds + r * (D * G::kEsz) + ((c ^ swz<G::kCPR>(r)) * 16) + w));
+  return load_op<T>((const T*)(blk + r * (D * esz) + ((c ^ swz<cpr>(r)) * 16) + w));
 }
 
-// B operand of the second GEMM from the slot-packed LDS part: 32-block `blk` of the stage, d-block db, group g.
+// B operand of the gradient GEMM from a slot-packed LDS block: d-block db, group g.
 template <typename T, int D>
-__device__ inline typename Elem<T>::Op lds_b(const char* lds, int blk, int db, int g, int lane) {
-  using G = StageGeom<T, D>;
-  const T* p = (const T*)(lds + G::kPartBytes) + (int64_t)blk * 32 * D + slot_off<T>(D, db, g, lane);
-  return load_op<T>(p);
+__device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int lane) {
+  return load_op<T>((const T*)blk + slot_off<T>(D, db, g, lane));
 }
+
+// Epilogue of the forward sweep for one 32x32 tile (16 values per lane). With
+//   softplus(z) = max(z,0) + ln(1 + e^-|z|) = ln 2 + z/2 + [ |z|/2 + ln((1 + e^-|z|) / 2) ],
+// e_acc gathers the bracket (it is 0 for z = 0, so zero padding adds nothing), 16 logits at a time as
+// sum|z|/2 + ln 2 * (log2(prod(1 + e^-|z|)) - 16); z/2 and ln 2 are added back per row in float64.
+// With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives) = sign(z) (1/(1+e^-|z|) - 1/2).
+template <bool GRAD, bool HASPOS>
+__device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e_acc, float& posz) {
+  float s1 = 0.f, prod = 1.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float zi = z[i];
+    const float az = __builtin_fabsf(zi);
+    const float tt = __builtin_amdgcn_exp2f(az * -kLog2e);
+    const float w1 = 1.f + tt;
+    prod *= w1;
+    s1 += az;
+    if (GRAD) c[i] = __builtin_copysignf(__builtin_amdgcn_rcpf(w1) - 0.5f, zi);
+  }
+  e_acc += 0.5f * s1 + kLn2 * (__builtin_amdgcn_logf(prod) - 16.f);
+  if (HASPOS) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (pm & (1u << i)) {
+        posz += z[i];
+        if (GRAD) c[i] -= 1.f;
+      }
+  }
+}
+
+// Epilogue of the backward sweep: c = sigma(z) - 1/2 = 1/(1 + e^-z) - 1/2 (minus 1 at positives); e^-z may
+// overflow to +inf, which gives exactly -1/2.
+template <bool HASPOS>
+__device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float tt = __builtin_amdgcn_exp2f(z[i] * -kLog2e);
+    c[i] = __builtin_amdgcn_rcpf(1.f + tt) - 0.5f;
+  }
+  if (HASPOS) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (pm & (1u << i)) c[i] -= 1.f;
+  }
+}
+
+// Interleave hint for one pipelined iteration: LDS reads first, then each MFMA preceded by a share of the
+// epilogue's VALU work.
+template <int NMFMA, int VPM>
+__device__ inline void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);  // DS reads
+#pragma unroll
+  for (int k = 0; k < NMFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// The step engine. Owner operands (H rows in the forward, E items in the backward) sit in registers; the
+// streamed matrix X (E or Hc) and its slot-packed copy Xsp flow through the LDS rings.
+//   FWD: epilogue = softplus (+ sigma with GRAD), owner = rows; !FWD: epilogue = sigma, owner = items.
+// Runs steps [j0, j1) of 32 streamed rows; bucket pointers of step j are bptr[bbase + j], bptr[bbase + j + 1].
+// Iteration i issues the logit GEMM of step i+1 and the gradient GEMM of step i-1 (with the G of step i-1,
+// packed at the end of iteration i-1) and evaluates the epilogue of step i; none of the three depends on
+// another inside the iteration. Ring schedule (step j, ring depth N): its d-packed block is loaded at
+// iteration j - N into slot j % N and read at iteration j - 1; its slot-packed block is loaded at iteration
+// j - N + 2 into slot j % N and read at iteration j + 1. One barrier starts every iteration.
+// ---------------------------------------------------------------------------------------------------------
+template <typename T, int D, int NW, bool FWD, bool GRAD>
+struct Engine {
+  using EL = Elem<T>;
+  using G = Geo<T, D, NW, GRAD>;
+  static constexpr int KS = D / EL::kK, NDB = D / 32;
+  using Op = typename EL::Op;
+
+  char* lds;
+  int wave, lane;
+  const T* X;
+  const T* Xsp;
+  int64_t nX;
+  const int32_t* bptr;
+  const int2* pairs;
+  int64_t bbase;
+  int own0;  // first owner index of this wave (compact row or item)
+  int j0, j1;
+
+  __device__ inline char* ringA(int rel) const { return lds + (rel % G::kNA) * G::kStepBytes; }
+  __device__ inline char* ringB(int rel) const {
+    return lds + (G::kNA + rel % (G::kNB ? G::kNB : 1)) * G::kStepBytes;
+  }
+  __device__ inline uint32_t* lmask() const {
+    return (uint32_t*)(lds + (G::kNA + G::kNB) * G::kStepBytes) + wave * 64;
+  }
+  __device__ inline int clampj(int rel) const { return j0 + rel < j1 ? j0 + rel : j1 - 1; }
+
+  // d-packed block of step j0 + rel into A slot rel % NA (rows >= nX read as zero).
+  __device__ inline void dma_a(int rel) const {
+    const int64_t row0 = (int64_t)clampj(rel) * 32;
+    const char* xa = (const char*)X + row0 * (int64_t)(D * G::kEsz);
+    const int64_t rem = (nX - row0) * (int64_t)(D * G::kEsz);
+    const int nrec = rem <= 0 ? 0 : (rem > (int64_t)G::kStepBytes ? G::kStepBytes : (int)rem);
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)xa, (short)0, nrec, 0x00020000);
+    char* dst = ringA(rel);
+#pragma unroll
+    for (int q = 0; q < G::kLoadsPerPart; ++q) {
+      const int inst = wave + q * NW;                           // wave instruction index within the block
+      const int pos = inst * G::kWaveBytes + lane * G::kLoadB;  // LDS byte written by this lane
+      const int row = pos / (D * G::kEsz);
+      const int within = pos % (D * G::kEsz);
+      const int lchunk = (within / 16) ^ swz<G::kCPR>(row);
+      const int voff = row * (D * G::kEsz) + lchunk * 16 + within % 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + inst * G::kWaveBytes), G::kLoadB, voff, 0, 0,
+                                               0);
+    }
+  }
+  // slot-packed block of step j0 + rel into B slot rel % NB (a contiguous copy).
+  __device__ inline void dma_b(int rel) const {
+    const int64_t row0 = (int64_t)clampj(rel) * 32;
+    const char* xb = (const char*)Xsp + row0 * (int64_t)(D * G::kEsz);
+    __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, G::kStepBytes, 0x00020000);
+    char* dst = ringB(rel);
+#pragma unroll
+    for (int q = 0; q < G::kLoadsPerPart; ++q) {
+      const int inst = wave + q * NW;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + inst * G::kWaveBytes), G::kLoadB,
+                                               inst * G::kWaveBytes + lane * G::kLoadB, 0, 0, 0);
+    }
+  }
+  __device__ inline int bucket(int rel) const { return bptr[bbase + (j0 + rel < j1 ? j0 + rel : j1)]; }
+
+  // Runs the sweep; `own` holds the owner operand for every k-step. On return acc holds the gradient tile
+  // (GRAD) and e_acc / posz the forward row sums (FWD).
+  __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz) {
+    const int n = j1 - j0;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // everyone is done with the previous unit's rings
+#pragma unroll
+    for (int q = 0; q < G::kNA; ++q) dma_a(q);
+    if (GRAD) {
+#pragma unroll
+      for (int q = 0; q + 2 < G::kNB; ++q) dma_b(q);
+    }
+    int bq[4];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) bq[q] = bucket(q);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    f32x16 za = f32x16{}, zb;  // logit tiles of the current and the next step, alternating roles
+    {
+      const char* a = ringA(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) za = EL::mma(lds_a<T, D>(a, lane % 32, ks, lane), own[ks], za);
+    }
+    GPack<T> gp;  // G of the previous step
+    iter<false>(0, own, acc, za, zb, gp, bq, e_acc, posz);
+    int i = 1;
+    for (; i + 1 < n; i += 2) {
+      iter<true>(i, own, acc, zb, za, gp, bq, e_acc, posz);
+      iter<true>(i + 1, own, acc, za, zb, gp, bq, e_acc, posz);
+    }
+    if (i < n) {
+      iter<true>(i, own, acc, zb, za, gp, bq, e_acc, posz);
+    }
+    if (GRAD) {  // gradient GEMM of the last step
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const char* b = ringB(n - 1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(b, db, g, lane), acc[db]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // One pipelined iteration i (see the ring schedule above). Positives only touch the 16 epilogue values, so
+  // the accumulators never cross a branch. PREV: a gradient GEMM of step i-1 exists (i > 0).
+  template <bool PREV>
+  __device__ inline void iter(int i, const Op* own, f32x16* acc, const f32x16& zc, f32x16& zn, GPack<T>& gp,
+                              int* bq, float& e_acc, float& posz) {
+    // Every wave has finished iteration i-1 (and the prologue's read of A slot 0 before iteration 0), so the
+    // slots about to be refilled are free; loads older than the previous iteration have landed.
+    wait_vm_and_barrier<G::kInFlight>();
+    dma_a(i + G::kNA);
+    if (GRAD) dma_b(i + G::kNB - 2);
+    bq[3] = bucket(i + 3);
+    const int pb = __builtin_amdgcn_readfirstlane(bq[0]);
+    const int pe = __builtin_amdgcn_readfirstlane(bq[1]);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) bq[q] = bq[q + 1];
+
+    const char* a = ringA(i + 1);
+    zn = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) zn = EL::mma(lds_a<T, D>(a, lane % 32, ks, lane), own[ks], zn);
+    if (GRAD && PREV) {
+      const char* b = ringB(i - 1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(b, db, g, lane), acc[db]);
+    }
+    float c[16];
+    if (FWD)
+      epi_rows<GRAD, false>(zc, 0u, c, e_acc, posz);
+    else
+      epi_items<false>(zc, 0u, c);
+    if (kUseHint) {
+      constexpr int nm = KS + ((GRAD && PREV) ? NDB * EL::kGroups : 0);
+      constexpr int valu = FWD ? (GRAD ? 150 : 90) : 80;
+      interleave_hint<nm, (valu + nm - 1) / nm>();
+    }
+    if (pe > pb) {
+      const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + i) * 32, FWD, lmask(), lane);
+      if (pm) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (pm & (1u << q)) {
+            if (FWD) posz += zc[q];
+            c[q] -= 1.f;
+          }
+      }
+    }
+    if (GRAD) gp.set(c);
+  }
+};
 
 struct RowsArgs {
   const void* Hc;
@@ -191,114 +417,52 @@ struct RowsArgs {
 template <typename T, int D, int NW, bool WITH_DH>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   using EL = Elem<T>;
-  using G = StageGeom<T, D>;
-  constexpr int NT = NW * 64, RW = NW * 32, KS = D / EL::kK, NDB = D / 32;
+  using EN = Engine<T, D, NW, true, WITH_DH>;
+  constexpr int RW = NW * 32, KS = D / EL::kK, NDB = D / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  uint32_t* lmask_all = (uint32_t*)(lds + 2 * G::kStageBytes);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-  uint32_t* lmask = lmask_all + wave * 64;
   const T* __restrict__ Hc = (const T*)a.Hc;
-  const T* __restrict__ E = (const T*)a.E;
-  const T* __restrict__ Evp = (const T*)a.Evp;
 
   const int n_valid = a.ctl->n_valid;
   const int Tt = (n_valid + RW - 1) / RW;
   if (Tt == 0) return;
-  const int n_stages = (int)(a.V_pad / G::kSI);
+  const int n_steps = (int)(a.V_pad / 32);
   const int P = gridDim.x;
-  const int S = choose_splits(Tt, n_stages, P, kMaxUnits);
+  const int S = choose_splits(Tt, n_steps, P);
   if (blockIdx.x == 0 && tid == 0) a.ctl->splits = S;
   const int U = Tt * S;
   const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int start = (int)(((int64_t)x * U) / 8), cnt = (int)(((int64_t)(x + 1) * U) / 8) - start;
 
+  EN en;
+  en.lds = lds;
+  en.wave = wave;
+  en.lane = lane;
+  en.X = (const T*)a.E;
+  en.Xsp = (const T*)a.Evp;
+  en.nX = a.V;
+  en.bptr = a.bptr;
+  en.pairs = a.pairs;
+
   for (int idx = slot; idx < cnt; idx += P / 8) {
     const int u = start + idx;
     const int s = u / Tt, t = u % Tt;
-    const int st0 = (int)(((int64_t)s * n_stages) / S), st1 = (int)(((int64_t)(s + 1) * n_stages) / S);
+    en.j0 = (int)(((int64_t)s * n_steps) / S);
+    en.j1 = (int)(((int64_t)(s + 1) * n_steps) / S);
     const int r_base = t * RW + wave * 32;
+    en.bbase = (int64_t)t * a.n_vs;
+    en.own0 = r_base;
 
     typename EL::Op hop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       hop[ks] = load_op<T>(Hc + (int64_t)(r_base + lane % 32) * D + ks * EL::kK + (lane / 32) * EL::kEPL);
     f32x16 acc[WITH_DH ? NDB : 1];
-    if (WITH_DH)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < (WITH_DH ? NDB : 1); ++db) acc[db] = f32x16{};
     float e_acc = 0.f, posz = 0.f;
 
-    Stager<T, D, NT, WITH_DH> pf;
-    constexpr int NSS = G::kSI / 32;
-    const int64_t bbase = (int64_t)t * a.n_vs;
-    __syncthreads();  // previous unit finished reading LDS
-    pf.load(E, Evp, (int64_t)st0 * G::kSI, a.V, tid);
-    pf.load_buckets(a.bptr, bbase + (int64_t)st0 * NSS);
-    pf.store(lds, tid);
-    __syncthreads();
-
-    for (int st = st0; st < st1; ++st) {
-      const char* buf = lds + ((st - st0) & 1) * G::kStageBytes;
-      const bool more = st + 1 < st1;
-      int bcur[NSS + 1];
-#pragma unroll
-      for (int j = 0; j <= NSS; ++j) bcur[j] = __builtin_amdgcn_readfirstlane(pf.bp[j]);
-      if (more) {
-        pf.load(E, Evp, (int64_t)(st + 1) * G::kSI, a.V, tid);
-        pf.load_buckets(a.bptr, bbase + (int64_t)(st + 1) * NSS);
-      }
-#pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) {
-        const int v0 = st * G::kSI + ss * 32;
-        typename EL::Op aop[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane);
-        f32x16 z = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], hop[ks], z);
-
-        const int pb = bcur[ss], pe = bcur[ss + 1];
-        uint32_t pm = 0u;
-        if (pe > pb) pm = positive_mask(a.pairs, pb, pe, r_base, v0, true, lmask, lane);
-
-        float c[16];
-        float s1 = 0.f, prod = 1.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float zi = z[i];
-          const float az = __builtin_fabsf(zi);
-          const float tt = __builtin_amdgcn_exp2f(az * -kLog2e);
-          const float w1 = 1.f + tt;
-          prod *= w1;
-          s1 += az;
-          if (WITH_DH) c[i] = __builtin_copysignf(__builtin_amdgcn_rcpf(w1) - 0.5f, zi);
-        }
-        e_acc += 0.5f * s1 + kLn2 * (__builtin_amdgcn_logf(prod) - 16.f);
-        if (pm) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (pm & (1u << i)) {
-              posz += z[i];
-              if (WITH_DH) c[i] -= 1.f;
-            }
-        }
-        if (WITH_DH) {
-          GPack<T> gp;
-          gp.set(c);
-          typename EL::Op bop[NDB][EL::kGroups];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < EL::kGroups; ++g) bop[db][g] = lds_b<T, D>(buf, ss, db, g, lane);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), bop[db][g], acc[db]);
-        }
-      }
-      if (more) pf.store(lds + ((st + 1 - st0) & 1) * G::kStageBytes, tid);
-      __syncthreads();
-    }
+    en.run(hop, acc, e_acc, posz);
 
     // unit results: per-row loss parts and the dH partial of this split
     const int64_t urow = (int64_t)u * RW + wave * 32;  // row of the unit-major partial buffers
@@ -334,13 +498,10 @@ struct ItemsArgs {
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   using EL = Elem<T>;
-  using G = StageGeom<T, D>;
-  constexpr int NT = NW * 64, IW = NW * 32, KS = D / EL::kK, NDB = D / 32;
+  using EN = Engine<T, D, NW, false, true>;
+  constexpr int IW = NW * 32, KS = D / EL::kK, NDB = D / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  uint32_t* lmask = (uint32_t*)(lds + 2 * G::kStageBytes) + (threadIdx.x / 64) * 64;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-  const T* __restrict__ Hc = (const T*)a.Hc;
-  const T* __restrict__ Hrp = (const T*)a.Hrp;
   const T* __restrict__ E = (const T*)a.E;
 
   const int t = blockIdx.x;
@@ -360,65 +521,23 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   const int n_valid = a.ctl->n_valid;
-  const int n_st = (n_valid + G::kSI - 1) / G::kSI;
-  Stager<T, D, NT, true> pf;
-  constexpr int NSS = G::kSI / 32;
-  const int64_t bbase = (int64_t)t * a.n_rs;
+  const int n_st = (n_valid + 31) / 32;
   if (n_st > 0) {
-    pf.load(Hc, Hrp, 0, (int64_t)n_valid, tid);
-    pf.load_buckets(a.bptr, bbase);
-    pf.store(lds, tid);
-  }
-  __syncthreads();
-  for (int st = 0; st < n_st; ++st) {
-    const char* buf = lds + (st & 1) * G::kStageBytes;
-    const bool more = st + 1 < n_st;
-    int bcur[NSS + 1];
-#pragma unroll
-    for (int j = 0; j <= NSS; ++j) bcur[j] = __builtin_amdgcn_readfirstlane(pf.bp[j]);
-    if (more) {
-      pf.load(Hc, Hrp, (int64_t)(st + 1) * G::kSI, (int64_t)n_valid, tid);
-      pf.load_buckets(a.bptr, bbase + (int64_t)(st + 1) * NSS);
-    }
-#pragma unroll
-    for (int ss = 0; ss < NSS; ++ss) {
-      const int r0 = st * G::kSI + ss * 32;
-      typename EL::Op aop[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(buf, ss * 32 + lane % 32, ks, lane);
-      f32x16 z = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], eop[ks], z);
-
-      const int pb = bcur[ss], pe = bcur[ss + 1];
-      uint32_t pm = 0u;
-      if (pe > pb) pm = positive_mask(a.pairs, pb, pe, (int)v_own0, r0, false, lmask, lane);
-
-      float c[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float tt = __builtin_amdgcn_exp2f(z[i] * -kLog2e);
-        c[i] = __builtin_amdgcn_rcpf(1.f + tt) - 0.5f;
-      }
-      if (pm) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (pm & (1u << i)) c[i] -= 1.f;
-      }
-      GPack<T> gp;
-      gp.set(c);
-      typename EL::Op bop[NDB][EL::kGroups];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < EL::kGroups; ++g) bop[db][g] = lds_b<T, D>(buf, ss, db, g, lane);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), bop[db][g], acc[db]);
-    }
-    if (more) pf.store(lds + ((st + 1) & 1) * G::kStageBytes, tid);
-    __syncthreads();
+    EN en;
+    en.lds = lds;
+    en.wave = wave;
+    en.lane = lane;
+    en.X = (const T*)a.Hc;
+    en.Xsp = (const T*)a.Hrp;
+    en.nX = n_valid;
+    en.bptr = a.bptr;
+    en.pairs = a.pairs;
+    en.bbase = (int64_t)t * a.n_rs;
+    en.own0 = (int)v_own0;
+    en.j0 = 0;
+    en.j1 = n_st;
+    float e_acc = 0.f, posz = 0.f;
+    en.run(eop, acc, e_acc, posz);
   }
 
   // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d])
@@ -444,7 +563,7 @@ static int g_cus = 0;
 static int cu_count() {
   if (g_cus == 0) {
     int dev = 0;
-    hipGetDevice(&dev);
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     g_cus = n;
@@ -454,7 +573,7 @@ static int cu_count() {
 
 template <typename T, int D, int NW, bool WITH_DH>
 static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st) {
-  using G = StageGeom<T, D>;
+  using G = Geo<T, D, NW, WITH_DH>;
   RowsArgs a;
   a.Hc = ws + L.off_Hc;
   a.E = E;
@@ -468,7 +587,7 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   a.R_pad = L.R_pad;
   a.dhpart = (float*)(ws + L.off_dhpart);
   a.rowpart = (float2*)(ws + L.off_rowpart);
-  const size_t sm = 2 * G::kStageBytes + NW * 64 * 4;
+  const size_t sm = G::kLdsBytes;
   auto kern = k_rows<T, D, NW, WITH_DH>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
@@ -480,7 +599,7 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
 template <typename T, int D, int NW>
 static hipError_t items_launch(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                                hipStream_t st) {
-  using G = StageGeom<T, D>;
+  using G = Geo<T, D, NW, true>;
   ItemsArgs a;
   a.Hc = ws + L.off_Hc;
   a.Hrp = ws + L.off_Hrp;
@@ -493,7 +612,7 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   a.dE = dE;
   a.V = L.V;
   a.n_rs = L.n_rs;
-  const size_t sm = 2 * G::kStageBytes + NW * 64 * 4;
+  const size_t sm = G::kLdsBytes;
   auto kern = k_items<T, D, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
