@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run a plain elementwise copy (torch.neg) of this many MiB three "
+                         "times: the known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
 
 
@@ -84,15 +87,21 @@ def cpu_baseline(prob, R_v, target_s):
 
 
 def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary; None when there is none or when the
+    kernel sources changed after the counters were taken."""
+    from vocabulary_label_bce_amd.profiling import source_digest
+
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             d = json.load(f)
-        return d.get("bytes_per_launch")
-    except Exception:
+    except (OSError, ValueError):
         return None
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("bytes_per_launch")
 
 
 def main():
@@ -183,6 +192,15 @@ def main():
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prob, R_v, a.cpu_seconds)
+    if a.copy_mib > 0:
+        n = a.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"kernel": "torch.neg float32", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                                   "launches": 3}
     print(json.dumps(out))
 
 

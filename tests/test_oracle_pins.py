@@ -268,8 +268,15 @@ def test_rejects_bad_ids():
 
 
 def test_dense_logits_size_matches_paper():
-    # Section I-A: 16 x 256 x 876,939 float32 logits take about 13.38 GiB.
-    assert W.dense_logits_bytes(16 * 256, 876_939) / 2 ** 30 == pytest.approx(13.38, abs=0.005)
+    # Section I-A of the paper prints the size of one local batch's float32 logits (tests/golden fixture).
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "paper_logits_size.json")))
+    b = W.dense_logits_bytes(g["batch"] * g["seq_len"], g["vocab"])
+    assert b == g["batch"] * g["seq_len"] * g["vocab"] * g["bytes_per_logit"]
+    assert b / 2 ** 30 == pytest.approx(g["gib_printed"], abs=0.005)
+    assert b / 2 ** 30 / 16 == pytest.approx(g["fraction_of_16_gib_printed"], abs=0.0005)
 
 
 PINS = [pin_elementwise, pin_zero_E, pin_zero_H, pin_finite_differences, pin_torch_dense]

@@ -1,0 +1,131 @@
+"""Turns rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+  python -m vocabulary_label_bce_amd.profiling stats --csv <dir>/run_kernel_stats.csv --out <file.md>
+      --title "..." --command "..."
+  python -m vocabulary_label_bce_amd.profiling traffic --fetch <dir>/run_counter_collection.csv
+      --write <dir>/run_counter_collection.csv --kernel-regex k_rows< --name rows_sweep --workload sasrec876k
+      --copy-regex neg_kernel --copy-bytes N --out <file.json> --command "..."
+
+`traffic` reads one FETCH_SIZE pass and one WRITE_SIZE pass (KiB per dispatch). It scales each counter by
+what the same counter read for a plain copy kernel that moved a known number of bytes in the same run, so the
+result is in HBM bytes per launch. The JSON records a digest of the kernel sources, and a reader treats the
+figure as stale once the sources differ.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the library's kernel sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path, counter):
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                yield row["Kernel_Name"], float(row["Counter_Value"]), int(row["Dispatch_Id"])
+
+
+def _per_dispatch(path, counter, regex):
+    """Counter value of each dispatch whose kernel name matches regex (summed over duplicate records)."""
+    pat = re.compile(regex)
+    acc = {}
+    for name, val, disp in _counter_rows(path, counter):
+        if pat.search(name):
+            acc[disp] = acc.get(disp, 0.0) + val
+    return [acc[k] for k in sorted(acc)]
+
+
+def traffic(fetch_csv, write_csv, kernel_regex, copy_regex, copy_bytes):
+    fk = _per_dispatch(fetch_csv, "FETCH_SIZE", kernel_regex)
+    wk = _per_dispatch(write_csv, "WRITE_SIZE", kernel_regex)
+    fc = _per_dispatch(fetch_csv, "FETCH_SIZE", copy_regex)
+    wc = _per_dispatch(write_csv, "WRITE_SIZE", copy_regex)
+    if not (fk and wk and fc and wc):
+        raise SystemExit(f"missing dispatches: kernel fetch {len(fk)} write {len(wk)}, copy fetch {len(fc)} "
+                         f"write {len(wc)}")
+    # copy kernel: reads copy_bytes and writes copy_bytes
+    f_fetch = copy_bytes / (statistics.median(fc) * 1024.0)
+    f_write = copy_bytes / (statistics.median(wc) * 1024.0)
+    fetch_b = statistics.median(fk) * 1024.0 * f_fetch
+    write_b = statistics.median(wk) * 1024.0 * f_write
+    return {
+        "fetch_kib_per_dispatch": [round(x, 1) for x in fk],
+        "write_kib_per_dispatch": [round(x, 1) for x in wk],
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": [round(x, 1) for x in fc],
+        "copy_write_kib": [round(x, 1) for x in wc],
+        "scale_fetch": f_fetch,
+        "scale_write": f_write,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b,
+    }
+
+
+def stats_table(path, top=16):
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[3])
+    out = ["| kernel | calls | avg us | % of GPU time |", "|---|---|---|---|"]
+    for name, calls, avg, pct in rows[:top]:
+        out.append(f"| `{name[:80]}` | {calls} | {avg:.1f} | {pct:.2f} |")
+    return "\n".join(out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--note", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel-regex", required=True)
+    t.add_argument("--name", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-regex", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", action="append", default=[])
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        txt = [f"# {a.title}", "", "Command (repo root, on the MI355X box):", "", "```", a.command, "```", "",
+               f"Source: `{os.path.basename(a.csv)}`.", "", stats_table(a.csv), ""]
+        if a.note:
+            txt += [a.note, ""]
+        with open(a.out, "w") as f:
+            f.write("\n".join(txt))
+    else:
+        d = traffic(a.fetch, a.write, a.kernel_regex, a.copy_regex, a.copy_bytes)
+        d.update({"kernel": a.name, "kernel_regex": a.kernel_regex, "workload": a.workload,
+                  "source_digest": source_digest(), "commands": a.command})
+        with open(a.out, "w") as f:
+            json.dump(d, f, indent=1)
+        print(json.dumps({k: d[k] for k in ("kernel", "bytes_per_launch", "scale_fetch", "scale_write")}))
+
+
+if __name__ == "__main__":
+    main()
