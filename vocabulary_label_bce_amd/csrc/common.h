@@ -89,7 +89,7 @@ struct Layout {
   size_t total;
 };
 
-constexpr int kEBlkItems = 2048;  // items per block of the E preparation kernel (column-sum granularity)
+constexpr int kEBlkItems = 256;   // items per block of the E preparation kernel (column-sum granularity)
 constexpr int kScanBlock = 8192;  // elements per block of the multi-block scan
 
 // Launch configuration of the two sweeps for a (dtype, D): waves per workgroup.

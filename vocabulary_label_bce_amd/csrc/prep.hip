@@ -88,6 +88,19 @@ hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const 
   return hipGetLastError();
 }
 
+// One slot-packed run (see slot_off) gathered from a [32][D] tile in LDS.
+template <typename T>
+__device__ inline void set_run(typename Elem<T>::Op& run, const T* tile, int D, int db, int g, int lane);
+template <>
+__device__ inline void set_run<__bf16>(bf16x8& run, const __bf16* tile, int D, int db, int g, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) run[j] = tile[acc_pos(g * 8 + j, lane / 32) * D + db * 32 + lane % 32];
+}
+template <>
+__device__ inline void set_run<float>(float& run, const float* tile, int D, int db, int g, int lane) {
+  run = tile[acc_pos(g, lane / 32) * D + db * 32 + lane % 32];
+}
+
 // ---------------------------------------------------------------------------------------------------------
 // H preparation: block = 32 compacted rows. Hc[k] = H[row_of[k]] (0 for padding), Hrp = slot-packed Hc
 // blocks, per-block column sums (float64) of the valid rows.
@@ -117,9 +130,9 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
     for (int q = tid; q < runs; q += 256) {
       const int lane = q % 64, g = (q / 64) % Elem<T>::kGroups, db = q / (64 * Elem<T>::kGroups);
       const int64_t o = slot_off<T>(D, db, g, lane);
-#pragma unroll
-      for (int j = 0; j < Elem<T>::kEPL; ++j)
-        dst[o + j] = tile[acc_pos(g * Elem<T>::kEPL + j, lane / 32) * D + db * 32 + lane % 32];
+      typename Elem<T>::Op run;
+      set_run<T>(run, tile, D, db, g, lane);
+      *(typename Elem<T>::Op*)(dst + o) = run;
     }
   }
   for (int d = tid; d < D; d += 256) {
@@ -129,13 +142,24 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
   }
 }
 
-// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order.
-__global__ void k_sum_parts(const double* __restrict__ part, int64_t nparts, int D, double* __restrict__ out) {
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= D) return;
+// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order: block = 32 columns x 8 part lanes; part
+// lane y adds parts y, y + 8, y + 16, ... in order, then the 8 lane sums are added in order of y.
+__global__ void __launch_bounds__(256) k_sum_parts(const double* __restrict__ part, int64_t nparts, int D,
+                                                   double* __restrict__ out) {
+  __shared__ double sh[8][32];
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  const int d = blockIdx.x * 32 + tx;
   double s = 0.0;
-  for (int64_t p = 0; p < nparts; ++p) s += part[p * D + d];
-  out[d] = s;
+  if (d < D)
+    for (int64_t p = ty; p < nparts; p += 8) s += part[p * D + d];
+  sh[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && d < D) {
+    double t = 0.0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) t += sh[y][tx];
+    out[d] = t;
+  }
 }
 
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st) {
@@ -152,7 +176,7 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 255) / 256), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(256), 0, st,
                      (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
   return hipGetLastError();
 }
@@ -185,12 +209,9 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
       for (int q = tid; q < runs; q += 256) {
         const int lane = q % 64, g = (q / 64) % Elem<T>::kGroups, db = q / (64 * Elem<T>::kGroups);
         const int64_t o = slot_off<T>(D, db, g, lane);
-        T tmp[Elem<T>::kEPL];
-#pragma unroll
-        for (int j = 0; j < Elem<T>::kEPL; ++j)
-          tmp[j] = tile[acc_pos(g * Elem<T>::kEPL + j, lane / 32) * D + db * 32 + lane % 32];
-#pragma unroll
-        for (int j = 0; j < Elem<T>::kEPL; ++j) dst[o + j] = tmp[j];
+        typename Elem<T>::Op run;  // kEPL consecutive elements: one 16-byte (bf16) or 4-byte (f32) store
+        set_run<T>(run, tile, D, db, g, lane);
+        *(typename Elem<T>::Op*)(dst + o) = run;
       }
     }
     if (tid < D)
@@ -214,7 +235,7 @@ hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 255) / 256), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(256), 0, st,
                      (const double*)(ws + L.off_sumE_part), L.n_eblk, L.D, (double*)(ws + L.off_sumE));
   return hipGetLastError();
 }

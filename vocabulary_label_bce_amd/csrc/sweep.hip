@@ -25,10 +25,6 @@ namespace cutbce {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-#ifndef CUTBCE_SCHED_HINT
-#define CUTBCE_SCHED_HINT 0
-#endif
-constexpr bool kUseHint = CUTBCE_SCHED_HINT != 0;
 
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
@@ -128,24 +124,40 @@ __device__ inline int choose_splits(int T, int n_steps, int P) {
 
 // ---------------------------------------------------------------------------------------------------------
 // Geometry of the step engine for (T, D, NW waves, GRAD = gradient GEMM present).
+//
+// The streamed operand moves through two LDS rings, one 32-row block per step: the d-packed block of step j
+// (A, read for the logit GEMM during iteration j - 1) and its slot-packed copy (B, read by the gradient GEMM
+// during iteration j + 1). Workgroup barriers come every kK iterations (at iterations that are multiples of
+// kK), so that between two barriers the waves drift apart freely and one wave's vector work overlaps
+// another's MFMAs. With kS = 1 a barrier waits for all loads but those issued in the iteration just before
+// it. Then:
+//   A(j) is loaded at iteration j - kLA into slot j % kNA; B(j) at iteration j - kLB into slot j % kNB, with
+//   kLA >= kK + 1 + kS, kLB >= kK - 1 + kS     (a barrier separates landing from reading),
+//   kNA >= kLA + kK - 1, kNB >= kLB + kK + 1     (a barrier separates the last read of a slot from its
+//                                                 refill).
 // ---------------------------------------------------------------------------------------------------------
+#ifndef CUTBCE_STEPS_PER_BARRIER
+#define CUTBCE_STEPS_PER_BARRIER 0  // 0: by step size
+#endif
 template <typename T, int D, int NW, bool GRAD>
 struct Geo {
   static constexpr int kEsz = sizeof(T);
-  static constexpr int kStepBytes = 32 * D * kEsz;               // one 32-row block of an operand
-  static constexpr int kRing = kStepBytes <= 16384 ? 3 : 2;      // depth of each operand ring
-  static constexpr int kNA = kRing, kNB = GRAD ? kRing : 0;
-  static constexpr int kCPR = D * kEsz / 16;                     // 16-byte chunks per d-packed row
+  static constexpr int kStepBytes = 32 * D * kEsz;  // one 32-row block of an operand
+  static constexpr int kK = CUTBCE_STEPS_PER_BARRIER > 0 ? (kStepBytes <= 8192 ? CUTBCE_STEPS_PER_BARRIER : 1)
+                            : (kStepBytes <= 4096 ? 4 : kStepBytes <= 8192 ? 2 : 1);
+  static constexpr int kS = kStepBytes <= 16384 ? 1 : 0;
+  static constexpr int kLA = kK + 1 + kS, kLB = kK - 1 + kS;
+  static constexpr int kNA = kLA + kK - 1, kNB = GRAD ? kLB + kK + 1 : 0;
+  static constexpr int kCPR = D * kEsz / 16;                         // 16-byte chunks per d-packed row
   static constexpr int kLoadB = (kStepBytes / NW >= 1024) ? 16 : 4;  // bytes per lane per DMA load
-  static constexpr int kWaveBytes = 64 * kLoadB;                 // bytes one wave instruction moves
+  static constexpr int kWaveBytes = 64 * kLoadB;                     // bytes one wave instruction moves
   static constexpr int kLoadsPerPart = kStepBytes / kWaveBytes / NW;
   static constexpr int kLoadsPerIter = kLoadsPerPart * (GRAD ? 2 : 1) + 1;  // + the bucket-pointer load
-  // loads that may stay in flight at the top of an iteration: a 3-deep ring lets the previous iteration's
-  // loads land one iteration later; a 2-deep ring needs them now
-  static constexpr int kInFlight = kRing >= 3 ? kLoadsPerIter : 0;
+  static constexpr int kInFlight = kS ? kLoadsPerIter : 0;  // loads a barrier lets stay in flight
   static constexpr int kLdsBytes = (kNA + kNB) * kStepBytes + NW * 256;
   static_assert(kLoadsPerPart >= 1 && kStepBytes % (kWaveBytes * NW) == 0, "load split");
   static_assert(kLoadsPerIter <= 63, "vmcnt range");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
 // Ring barrier. vmcnt(N): this wave's DMA loads older than the last N have landed in LDS. lgkmcnt(0): this
@@ -179,18 +191,24 @@ __device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int
 // With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives) = sign(z) (1/(1+e^-|z|) - 1/2).
 template <bool GRAD, bool HASPOS>
 __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e_acc, float& posz) {
-  float s1 = 0.f, prod = 1.f;
+  // u_i = -|z_i| log2(e); 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow. Pairwise
+  // products and sums keep the dependency chains short.
+  float u[16], w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float zi = z[i];
-    const float az = __builtin_fabsf(zi);
-    const float tt = __builtin_amdgcn_exp2f(az * -kLog2e);
-    const float w1 = 1.f + tt;
-    prod *= w1;
-    s1 += az;
-    if (GRAD) c[i] = __builtin_copysignf(__builtin_amdgcn_rcpf(w1) - 0.5f, zi);
+    u[i] = __builtin_fabsf(z[i]) * -kLog2e;
+    w[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
+    if (GRAD) c[i] = __builtin_copysignf(__builtin_amdgcn_rcpf(w[i]) - 0.5f, z[i]);
   }
-  e_acc += 0.5f * s1 + kLn2 * (__builtin_amdgcn_logf(prod) - 16.f);
+#pragma unroll
+  for (int h = 8; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      w[i] *= w[i + h];
+      u[i] += u[i + h];
+    }
+  // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2] = ln 2 * (log2(prod) - 16 - sum_i u_i / 2)
+  e_acc += kLn2 * (__builtin_amdgcn_logf(w[0]) - 16.f - 0.5f * u[0]);
   if (HASPOS) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -215,19 +233,6 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
     for (int i = 0; i < 16; ++i)
       if (pm & (1u << i)) c[i] -= 1.f;
   }
-}
-
-// Interleave hint for one pipelined iteration: LDS reads first, then each MFMA preceded by a share of the
-// epilogue's VALU work.
-template <int NMFMA, int VPM>
-__device__ inline void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 64, 0);  // DS reads
-#pragma unroll
-  for (int k = 0; k < NMFMA; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-  }
-  __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -305,96 +310,102 @@ struct Engine {
 
   // Runs the sweep; `own` holds the owner operand for every k-step. On return acc holds the gradient tile
   // (GRAD) and e_acc / posz the forward row sums (FWD).
+  //
+  // Iteration i does the logit GEMM of step i and the gradient GEMM of step i-1 (with the G tile of step i-1)
+  // on the matrix cores, then reads the A operands of step i+1 and runs the epilogue of step i (giving G(i))
+  // on the vector ALU; none of these depends on another inside the iteration. Each wave keeps one logit tile,
+  // one G tile and the A operands of its next logit GEMM in registers. Barriers come only every kK
+  // iterations, so the waves of a SIMD drift apart and one wave's vector work overlaps another's MFMAs. A last
+  // iteration i = n finishes the pipeline (no loads, no logit GEMM).
   __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz) {
     const int n = j1 - j0;
+    if (n <= 0) return;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // everyone is done with the previous unit's rings
 #pragma unroll
-    for (int q = 0; q < G::kNA; ++q) dma_a(q);
+    for (int q = 0; q < G::kLA; ++q) dma_a(q);
     if (GRAD) {
 #pragma unroll
-      for (int q = 0; q + 2 < G::kNB; ++q) dma_b(q);
+      for (int q = 0; q < G::kLB; ++q) dma_b(q);
     }
     int bq[4];
 #pragma unroll
     for (int q = 0; q < 3; ++q) bq[q] = bucket(q);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-    f32x16 za = f32x16{}, zb;  // logit tiles of the current and the next step, alternating roles
-    {
-      const char* a = ringA(0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) za = EL::mma(lds_a<T, D>(a, lane % 32, ks, lane), own[ks], za);
+    Op aop[KS];  // A operands of the next logit GEMM
+    f32x16 z;    // logit tile whose epilogue is pending
+    GPack<T> g;  // G tile whose gradient GEMM is pending
+    read_a(0, aop);
+    top(0);
+    z = logits(aop, own);
+    read_a(1, aop);
+    epilogue(0, z, g, bq, e_acc, posz);
+    for (int i = 1; i < n; ++i) {
+      top(i);
+      z = logits(aop, own);
+      if (GRAD) grad(i - 1, g, acc);
+      read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
+      epilogue(i, z, g, bq, e_acc, posz);
     }
-    GPack<T> gp;  // G of the previous step
-    iter<false>(0, own, acc, za, zb, gp, bq, e_acc, posz);
-    int i = 1;
-    for (; i + 1 < n; i += 2) {
-      iter<true>(i, own, acc, zb, za, gp, bq, e_acc, posz);
-      iter<true>(i + 1, own, acc, za, zb, gp, bq, e_acc, posz);
-    }
-    if (i < n) {
-      iter<true>(i, own, acc, zb, za, gp, bq, e_acc, posz);
-    }
-    if (GRAD) {  // gradient GEMM of the last step
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      const char* b = ringB(n - 1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(b, db, g, lane), acc[db]);
-    }
+    // iteration n: the slot-packed block of step n-1 must have landed
+    wait_vm_and_barrier<0>();
+    if (GRAD) grad(n - 1, g, acc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  // One pipelined iteration i (see the ring schedule above). Positives only touch the 16 epilogue values, so
-  // the accumulators never cross a branch. PREV: a gradient GEMM of step i-1 exists (i > 0).
-  template <bool PREV>
-  __device__ inline void iter(int i, const Op* own, f32x16* acc, const f32x16& zc, f32x16& zn, GPack<T>& gp,
-                              int* bq, float& e_acc, float& posz) {
-    // Every wave has finished iteration i-1 (and the prologue's read of A slot 0 before iteration 0), so the
-    // slots about to be refilled are free; loads older than the previous iteration have landed.
-    wait_vm_and_barrier<G::kInFlight>();
-    dma_a(i + G::kNA);
-    if (GRAD) dma_b(i + G::kNB - 2);
-    bq[3] = bucket(i + 3);
+  // Start of iteration i: the barrier (every kK iterations) and the loads of the iteration.
+  __device__ inline void top(int i) {
+    if (G::kK == 1 || i % G::kK == 0) wait_vm_and_barrier<G::kInFlight>();
+    dma_a(i + G::kLA);
+    if (GRAD) dma_b(i + G::kLB);
+  }
+
+  __device__ inline void read_a(int i, Op* aop) const {
+    const char* a = ringA(i);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(a, lane % 32, ks, lane);
+  }
+
+  __device__ inline f32x16 logits(const Op* aop, const Op* own) const {
+    f32x16 z = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], own[ks], z);
+    return z;
+  }
+
+  __device__ inline void grad(int j, const GPack<T>& g, f32x16* acc) const {
+    const char* b = ringB(j);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q = 0; q < EL::kGroups; ++q) acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, db, q, lane), acc[db]);
+  }
+
+  // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step from the bucket FIFO,
+  // loss sums (FWD) and the G tile (GRAD).
+  __device__ inline void epilogue(int j, const f32x16& z, GPack<T>& g, int* bq, float& e_acc, float& posz) {
+    bq[3] = bucket(j + 3);
     const int pb = __builtin_amdgcn_readfirstlane(bq[0]);
     const int pe = __builtin_amdgcn_readfirstlane(bq[1]);
 #pragma unroll
     for (int q = 0; q < 3; ++q) bq[q] = bq[q + 1];
-
-    const char* a = ringA(i + 1);
-    zn = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) zn = EL::mma(lds_a<T, D>(a, lane % 32, ks, lane), own[ks], zn);
-    if (GRAD && PREV) {
-      const char* b = ringB(i - 1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < EL::kGroups; ++g) acc[db] = EL::mma(gp.op(g), lds_b<T, D>(b, db, g, lane), acc[db]);
-    }
     float c[16];
     if (FWD)
-      epi_rows<GRAD, false>(zc, 0u, c, e_acc, posz);
+      epi_rows<GRAD, false>(z, 0u, c, e_acc, posz);
     else
-      epi_items<false>(zc, 0u, c);
-    if (kUseHint) {
-      constexpr int nm = KS + ((GRAD && PREV) ? NDB * EL::kGroups : 0);
-      constexpr int valu = FWD ? (GRAD ? 150 : 90) : 80;
-      interleave_hint<nm, (valu + nm - 1) / nm>();
-    }
+      epi_items<false>(z, 0u, c);
     if (pe > pb) {
-      const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + i) * 32, FWD, lmask(), lane);
+      const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + j) * 32, FWD, lmask(), lane);
       if (pm) {
 #pragma unroll
         for (int q = 0; q < 16; ++q)
           if (pm & (1u << q)) {
-            if (FWD) posz += zc[q];
+            if (FWD) posz += z[q];
             c[q] -= 1.f;
           }
       }
     }
-    if (GRAD) gp.set(c);
+    if (GRAD) g.set(c);
   }
 };
 
@@ -591,7 +602,12 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   auto kern = k_rows<T, D, NW, WITH_DH>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  const int P = (cu_count() / 8) * 8;
+  // persistent: as many workgroups as can be resident at once, a multiple of 8 (one range per XCD)
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, NW * 64, sm) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int P = (cu_count() * per_cu / 8) * 8;
   hipLaunchKernelGGL(kern, dim3(P > 0 ? P : 8), dim3(NW * 64), sm, st, a);
   return hipGetLastError();
 }
