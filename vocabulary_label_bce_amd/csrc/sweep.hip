@@ -252,6 +252,7 @@ struct Engine {
   using G = Geo<T, D, NW, GRAD>;
   static constexpr int KS = D / EL::kK, NDB = D / 32;
   using Op = typename EL::Op;
+  static constexpr bool kPrefetch = KS * (int)sizeof(Op) <= 128;
 
   char* lds;
   int wave, lane;
@@ -332,26 +333,49 @@ struct Engine {
     for (int q = 0; q < 3; ++q) bq[q] = bucket(q);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-    Op aop[KS];  // A operands of the next logit GEMM
-    f32x16 z;    // logit tile whose epilogue is pending
     GPack<T> g;  // G tile whose gradient GEMM is pending
-    read_a(0, aop);
-    top(0);
-    z = logits(aop, own);
-    read_a(1, aop);
-    epilogue(0, z, g, bq, e_acc, posz);
-    for (int i = 1; i < n; ++i) {
-      top(i);
+    if constexpr (kPrefetch) {
+      // A operands of the next logit GEMM read a step ahead (they fit in 32 registers per lane); one logit tile
+      Op aop[KS];
+      f32x16 z;  // logit tile whose epilogue is pending
+      read_a(0, aop);
+      top(0);
       z = logits(aop, own);
-      if (GRAD) grad(i - 1, g, acc);
-      read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
-      epilogue(i, z, g, bq, e_acc, posz);
+      read_a(1, aop);
+      epilogue(0, z, g, bq, e_acc, posz);
+      for (int i = 1; i < n; ++i) {
+        top(i);
+        z = logits(aop, own);
+        if (GRAD) grad(i - 1, g, acc);
+        read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
+        epilogue(i, z, g, bq, e_acc, posz);
+      }
+    } else {
+      // larger D: the logit GEMM of step i+1 runs in iteration i, reading its A operands from LDS right before
+      // each MFMA; two logit tiles alternate roles
+      f32x16 za = logits_lds(0, own), zb;
+      int i = 0;
+      for (; i + 1 < n; i += 2) {
+        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz);
+        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz);
+      }
+      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz);
     }
     // iteration n: the slot-packed block of step n-1 must have landed
     wait_vm_and_barrier<0>();
     if (GRAD) grad(n - 1, g, acc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+
+  // Iteration i of the larger-D schedule: Z(i+1) into zn, gradient GEMM of step i-1, epilogue of step i (zc).
+  __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GPack<T>& g, f32x16* acc,
+                                  int* bq, float& e_acc, float& posz) {
+    top(i);
+    if (i + 1 < n_steps()) zn = logits_lds(i + 1, own);
+    if (GRAD && i > 0) grad(i - 1, g, acc);
+    epilogue(i, zc, g, bq, e_acc, posz);
+  }
+  __device__ inline int n_steps() const { return j1 - j0; }
 
   // Start of iteration i: the barrier (every kK iterations) and the loads of the iteration.
   __device__ inline void top(int i) {
@@ -370,6 +394,13 @@ struct Engine {
     f32x16 z = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) z = EL::mma(aop[ks], own[ks], z);
+    return z;
+  }
+  __device__ inline f32x16 logits_lds(int i, const Op* own) const {
+    const char* a = ringA(i);
+    f32x16 z = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) z = EL::mma(lds_a<T, D>(a, lane % 32, ks, lane), own[ks], z);
     return z;
   }
 
