@@ -5,7 +5,8 @@ It shares no code with the GPU library (``vocabulary_label_bce_amd``) and never 
 
 The arithmetic lives in ``cutbce_oracle.c`` (plain C, float64, OpenMP over rows/items); this module only
 compiles it with gcc and marshals arrays. See the header of the C file for the equations it follows
-("Cut Binary Cross Entropy", Section III-A Eq. (1)-(3) and Section III-B Eq. (4)).
+("Cut Binary Cross Entropy", Section III-A Eq. (1)-(3), Section III-B Eq. (4) and the Cut Metrics of
+Section III-D).
 """
 from __future__ import annotations
 
@@ -52,7 +53,8 @@ def _load(plant: int = 0):
         lib.oracle_rows.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp, vp]
         lib.oracle_items.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
         lib.oracle_full.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp, vp]
-        for f in (lib.oracle_rows, lib.oracle_items, lib.oracle_full, lib.oracle_num_threads):
+        lib.oracle_metrics.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
+        for f in (lib.oracle_rows, lib.oracle_items, lib.oracle_full, lib.oracle_metrics, lib.oracle_num_threads):
             f.restype = ctypes.c_int
         _libs[plant] = lib
         return lib
@@ -147,3 +149,19 @@ def items(H, E, row_offsets, item_ids, row_mask, items, g: float = 1.0, plant: i
                                    it.size, _ptr(it), _ptr(dE))
     _check(st)
     return dict(dE=dE)
+
+
+def metrics(H, E, row_offsets, item_ids, row_mask, rows=None, eps: float = 0.0, plant: int = 0):
+    """Cut Metrics per row: int64 [n, 5] = TP, FP, FN, TN (prediction z > 0) and #{v : |z| <= eps}.
+    All rows when `rows` is None; masked rows give zeros."""
+    h, e, dt, R, V, D, ro, ids, m = _prep(H, E, row_offsets, item_ids, row_mask)
+    if rows is None:
+        rr, n, rp = None, R, None
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n, rp = rr.size, _ptr(rr)
+    out = np.zeros((n, 5), np.int64)
+    st = _load(plant).oracle_metrics(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m), float(eps),
+                                     n, rp, _ptr(out))
+    _check(st)
+    return out

@@ -25,6 +25,11 @@
  *   - R_v = 0 (every row masked) gives loss 0 and zero gradients;
  *   - row_loss[r] is the unnormalised sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
  *
+ * Cut Metrics (Section III-D): per position, the confusion counts TP, FP, FN, TN over the V items, computed
+ * from the same logits without materialising them. The section names no threshold; the plain reading used
+ * here is "predict positive iff sigma(z) > 1/2", i.e. iff z > 0 (z = 0 is a negative prediction). Masked rows
+ * get all-zero counts.
+ *
  * Inputs H and E are read either as IEEE float32 or as bfloat16 (dtype 0 / 1), each element converted
  * exactly to double before use.
  */
@@ -272,4 +277,58 @@ int oracle_full(int64_t R, int64_t V, int D, int dtype, const void *H, const voi
     }
     if (!row_loss) free(rl);
     return st;
+}
+
+/*
+ * Cut Metrics (Section III-D) for each requested row (all R when rows == NULL): out[i][0..4] =
+ * TP, FP, FN, TN with the prediction "z > 0", and the number of items with |z| <= eps (logits whose sign a
+ * lower-precision evaluation may decide differently). Masked rows get zeros.
+ */
+int oracle_metrics(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
+                   const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double eps,
+                   int64_t n_rows, const int64_t *rows, int64_t *out) {
+    int64_t rv;
+    int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
+    if (st) return st;
+    if (!rows) n_rows = R;
+    int err = 0;
+#pragma omp parallel
+    {
+        uint8_t *ymap = (uint8_t *)calloc((size_t)V, 1);
+        if (!ymap) {
+#pragma omp atomic write
+            err = OR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (!ymap) continue;
+            int64_t r = rows ? rows[i] : i;
+            int64_t *o = out + (size_t)i * 5;
+            for (int q = 0; q < 5; ++q) o[q] = 0;
+            if (r < 0 || r >= R) {
+#pragma omp atomic write
+                err = OR_BAD_SHAPE;
+                continue;
+            }
+            if (!row_mask[r]) continue;
+            mark_row(row_offsets, item_ids, r, ymap, 1);
+            for (int64_t v = 0; v < V; ++v) {
+                double z = dot_rv(H, E, dtype, r, v, D);
+#if ORACLE_PLANT == 6
+                int pred = z >= 0.0; /* planted: a zero logit predicted positive */
+#else
+                int pred = z > 0.0;
+#endif
+                int y = ymap[v] != 0;
+                if (pred && y) ++o[0];
+                else if (pred && !y) ++o[1];
+                else if (!pred && y) ++o[2];
+                else ++o[3];
+                if (fabs(z) <= eps) ++o[4];
+            }
+            mark_row(row_offsets, item_ids, r, ymap, 0);
+        }
+        free(ymap);
+    }
+    return err;
 }
