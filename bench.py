@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--metrics", action="store_true",
+                    help="also count the Cut Metrics (TP/FP/FN/TN per row) in the forward sweep")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy (torch.neg) of this many MiB three "
                          "times: the known-size reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -127,7 +129,7 @@ def main():
     ro, ids, m = prob["row_offsets"], prob["item_ids"], prob["row_mask"]
     R_v = int(m.sum().item())
     V, D = E.shape
-    w = Workspace(H, E, ids, want_row_loss=False, save_dh=True)
+    w = Workspace(H, E, ids, want_row_loss=False, save_dh=True, want_metrics=a.metrics)
     g = torch.ones(1, dtype=torch.float32, device=dev)
 
     def step():
@@ -181,7 +183,7 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "N": cfg.N, "rows": cfg.R, "valid_rows": R_v, "D": D, "V": V,
-                   "nnz": int(ids.numel()), "global_batch": cfg.B, "seq_len": cfg.N},
+                   "nnz": int(ids.numel()), "global_batch": cfg.B, "seq_len": cfg.N, "cut_metrics": a.metrics},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "rows_V_per_s": R_v * V / (ms * 1e-3),
         "credited_flops_per_step": F,

@@ -80,10 +80,14 @@ cutbce_status cutbce_workspace_size(const cutbce_problem *p, size_t *bytes);
  *   dh_saved  (device) float [R][D] or NULL: when given, the same sweep also forms
  *             s * sum_v (sigma(z_rv) - y_rv) E[v] (the dH of Eq. (4) for g = 1; 0 for masked rows) so that
  *             cutbce_backward can return dH without recomputing the logits for it.
+ *   metrics   (device) int32 [R][4] or NULL: Cut Metrics (Section III-D), counted in the same sweep from the
+ *             same float32 logits: TP, FP, FN, TN over the V items of each valid row, an item being predicted
+ *             positive iff z_rv > 0 (the section names no threshold: sigma(z) > 1/2 is used); all four are 0
+ *             for masked rows. A repeated id counts once; ids outside [0, V) are not positives.
  */
 cutbce_status cutbce_forward(const cutbce_problem *p, const void *H, const void *E,
                              const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
-                             float *loss, float *row_loss, float *dh_saved,
+                             float *loss, float *row_loss, float *dh_saved, int32_t *metrics,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward (Section III-B, Eq. (4); the custom VJP recomputes logit tiles on chip).

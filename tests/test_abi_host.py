@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cutbce.h but not exported"
     assert set(B.EXPORTS) == set(names)
-    assert lib.cutbce_version() >= 100
+    assert lib.cutbce_version() >= 101
 
 
 def test_status_strings():
@@ -47,7 +47,7 @@ def test_workspace_has_no_rows_times_vocab_term(name):
     assert ws < 0.5 * W.dense_logits_bytes(cfg.R, cfg.V) or cfg.R * cfg.V < 1e7
 
 
-def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_bytes=None):
+def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_bytes=None, metrics=None):
     lib = B.lib()
     if ws_bytes is None:
         try:
@@ -56,7 +56,7 @@ def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_byt
             ws_bytes = 1 << 40
     vp = ctypes.c_void_p
     return lib.cutbce_forward(ctypes.byref(p), vp(H), vp(E), vp(ro), vp(ids), vp(mask), vp(loss), None, None,
-                              vp(ws), ws_bytes, None)
+                              vp(metrics) if metrics else None, vp(ws), ws_bytes, None)
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every case below fails a host check first
@@ -79,6 +79,8 @@ def test_forward_rejects_bad_arguments():
     assert _call_forward(bad_dtype, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 3
     neg_nnz = B.Problem(64, 4096, -1, 64, 1)
     assert _call_forward(neg_nnz, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 2
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE,
+                         metrics=FAKE + 2) == 4  # misaligned metrics
     # nnz > 0 needs item_ids
     assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=0, mask=FAKE, loss=FAKE, ws=FAKE) == 1
 

@@ -46,7 +46,7 @@ def lib():
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         P = ctypes.POINTER(Problem)
         L.cutbce_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
-        L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
         L.cutbce_profile_enable.argtypes = [i32]
@@ -98,11 +98,12 @@ def alloc_workspace(p: Problem, device) -> torch.Tensor:
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
 
 
-def forward(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row_loss, dh_saved, ws, stream=None):
-    """cutbce_forward on device tensors (outputs written in place)."""
+def forward(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row_loss, dh_saved, ws, stream=None,
+            metrics=None):
+    """cutbce_forward on device tensors (outputs written in place; metrics: int32 [R, 4] or None)."""
     _check(lib().cutbce_forward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
-                                _ptr(row_mask), _ptr(loss), _ptr(row_loss), _ptr(dh_saved), _ptr(ws),
-                                ws.numel() if ws is not None else 0, _stream(stream)))
+                                _ptr(row_mask), _ptr(loss), _ptr(row_loss), _ptr(dh_saved), _ptr(metrics),
+                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_saved, dH, dE, ws, stream=None):

@@ -72,6 +72,7 @@ Layout make_layout(const cutbce_problem* p) {
   L.off_Evp = take((size_t)L.V_pad * L.D * L.esz);
   L.off_dhpart = take(sizeof(float) * (size_t)part_rows * L.D);
   L.off_rowpart = take(sizeof(float) * 2 * (size_t)part_rows);
+  L.off_metpart = take(sizeof(int32_t) * 4 * (size_t)part_rows);
   L.off_rowloss = take(sizeof(double) * L.R_pad);
   L.off_dhtmp = take(sizeof(float) * (size_t)L.R * L.D);
   L.off_bptr_r = take(sizeof(int32_t) * (L.nb_r + 1));
@@ -123,9 +124,9 @@ void prof_end(ProfRec* r, hipStream_t st) {
   if (r && hipEventRecord(r->b, st) != hipSuccess) r->kind = -1;
 }
 
-hipError_t timed_rows(const Layout& L, char* ws, const void* E, bool with_dh, hipStream_t st) {
+hipError_t timed_rows(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
   ProfRec* r = prof_begin(0, st);
-  hipError_t e = launch_rows_sweep(L, ws, E, with_dh, st);
+  hipError_t e = launch_rows_sweep(L, ws, E, with_dh, met, st);
   prof_end(r, st);
   return e;
 }
@@ -159,7 +160,7 @@ cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E
 
 extern "C" {
 
-int cutbce_version(void) { return 100; }
+int cutbce_version(void) { return 101; }
 
 const char* cutbce_status_string(cutbce_status s) {
   switch (s) {
@@ -185,12 +186,14 @@ cutbce_status cutbce_workspace_size(const cutbce_problem* p, size_t* bytes) {
 
 cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
                              const int32_t* item_ids, const uint8_t* row_mask, float* loss, float* row_loss,
-                             float* dh_saved, void* workspace, size_t workspace_bytes, void* stream) {
+                             float* dh_saved, int32_t* metrics, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   Layout L;
   cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
   if (s != CUTBCE_OK) return s;
   if (!loss) return CUTBCE_ERR_NULL;
-  if (misaligned(dh_saved, 16) || misaligned(loss, 4) || misaligned(row_loss, 4)) return CUTBCE_ERR_ALIGN;
+  if (misaligned(dh_saved, 16) || misaligned(loss, 4) || misaligned(row_loss, 4) || misaligned(metrics, 4))
+    return CUTBCE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const bool with_dh = dh_saved != nullptr;
@@ -198,8 +201,8 @@ cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void*
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_prep_e(L, ws, E, with_dh, st));
   TRY(launch_buckets(L, ws, item_ids, true, st));
-  TRY(timed_rows(L, ws, E, with_dh, st));
-  TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, st));
+  TRY(timed_rows(L, ws, E, with_dh, metrics != nullptr, st));
+  TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, metrics, st));
   return CUTBCE_OK;
 }
 
@@ -229,8 +232,8 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
       float* tmp = (float*)(ws + L.off_dhtmp);
       TRY(launch_prep_e(L, ws, E, true, st));
       TRY(launch_buckets(L, ws, item_ids, true, st));
-      TRY(timed_rows(L, ws, E, true, st));
-      TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, st));
+      TRY(timed_rows(L, ws, E, true, false, st));
+      TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, nullptr, st));
       TRY(launch_scale_dh(L, tmp, grad_loss, dH, st));
     }
   }

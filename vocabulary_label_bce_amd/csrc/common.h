@@ -83,7 +83,7 @@ struct Layout {
   int64_t n_eblk;     // blocks of the E preparation kernel
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_Hc, off_Hrp, off_sumH, off_sumH_part;
-  size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_rowloss, off_dhtmp;
+  size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan;
   size_t scan_elems;
   size_t total;
@@ -105,9 +105,9 @@ hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const 
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st);
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st);
 hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st);
-hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, hipStream_t st);
+hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st);
 hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
-                              float* row_loss, float* dh_out, bool with_dh, hipStream_t st);
+                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, hipStream_t st);
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                               hipStream_t st);
 hipError_t launch_scale_dh(const Layout& L, const float* src, const float* grad_loss, void* dH, hipStream_t st);

@@ -7,6 +7,8 @@
 // "Cut Binary Cross Entropy" Eq. (2)-(3) is
 //   V ln 2 + (1/2) H[r].sum_v E[v] + sum_splits e - sum_splits p,
 // and dH[r] = s * (sum_splits dH_part + (1/2) sum_v E[v]) (Eq. (4) with sigma split as (sigma - 1/2) + 1/2).
+// With Cut Metrics (Section III-D) the sweep also leaves, per split, the counts of logits predicted positive
+// (z > 0), of positives predicted positive and of positives; TP, FP, FN and TN follow by subtraction.
 #include "common.h"
 
 namespace cutbce {
@@ -18,6 +20,11 @@ __device__ inline double wave_sum(double x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+__device__ inline int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl, const T* __restrict__ H,
@@ -25,14 +32,17 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
                                                      const int32_t* __restrict__ compact_of,
                                                      const float* __restrict__ dhpart,
                                                      const float2* __restrict__ rowpart,
+                                                     const int4* __restrict__ metpart,
                                                      const double* __restrict__ sumE, int64_t R, int64_t V, int D,
                                                      int RW, float* __restrict__ row_loss,
-                                                     double* __restrict__ rowloss_c, float* __restrict__ dh_out) {
+                                                     double* __restrict__ rowloss_c, float* __restrict__ dh_out,
+                                                     int32_t* __restrict__ metrics) {
   const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = lane_id();
   if (r >= R) return;
   if (mask[r] == 0) {
     if (row_loss && lane == 0) row_loss[r] = 0.f;
+    if (metrics && lane < 4) metrics[r * 4 + lane] = 0;
     if (dh_out)
       for (int d = lane; d < D; d += 64) dh_out[r * D + d] = 0.f;
     return;
@@ -60,6 +70,21 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
   e = wave_sum(e);
   p = wave_sum(p);
   zs = wave_sum(zs);
+  if (metrics) {
+    // Cut Metrics: predicted positive (z > 0), true positives, positives, summed over the splits
+    int np = 0, tp = 0, npos = 0;
+    for (int s = lane; s < S; s += 64) {
+      const int4 q = metpart[(int64_t)(s * Tt + t) * RW + loc];
+      np += q.x;
+      tp += q.y;
+      npos += q.z;
+    }
+    np = wave_sum_i(np);
+    tp = wave_sum_i(tp);
+    npos = wave_sum_i(npos);
+    const int fp = np - tp, fn = npos - tp, tn = (int)(V - tp - fp - fn);
+    if (lane < 4) metrics[r * 4 + lane] = lane == 0 ? tp : lane == 1 ? fp : lane == 2 ? fn : tn;
+  }
   const double rl = (double)V * 0.69314718055994530942 + 0.5 * zs + e - p;
   if (lane == 0) {
     if (row_loss) row_loss[r] = (float)rl;
@@ -84,19 +109,21 @@ __global__ void __launch_bounds__(1024) k_loss_final(const Ctl* __restrict__ ctl
 }
 
 hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
-                              float* row_loss, float* dh_out, bool with_dh, hipStream_t st) {
+                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, hipStream_t st) {
   const unsigned blocks = (unsigned)((L.R + 3) / 4);
   const Ctl* ctl = (const Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {
     hipLaunchKernelGGL(k_rows_finish<__bf16>, dim3(blocks), dim3(256), 0, st, ctl, (const __bf16*)H, mask,
                        (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
-                       (const float2*)(ws + L.off_rowpart), (const double*)(ws + L.off_sumE), L.R, L.V, L.D,
-                       L.rows_per_wg, row_loss, (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr);
+                       (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
+                       (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
+                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);
   } else {
     hipLaunchKernelGGL(k_rows_finish<float>, dim3(blocks), dim3(256), 0, st, ctl, (const float*)H, mask,
                        (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
-                       (const float2*)(ws + L.off_rowpart), (const double*)(ws + L.off_sumE), L.R, L.V, L.D,
-                       L.rows_per_wg, row_loss, (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr);
+                       (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
+                       (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
+                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;

@@ -246,7 +246,7 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // iteration j - N into slot j % N and read at iteration j - 1; its slot-packed block is loaded at iteration
 // j - N + 2 into slot j % N and read at iteration j + 1. One barrier starts every iteration.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool FWD, bool GRAD>
+template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false>
 struct Engine {
   using EL = Elem<T>;
   using G = Geo<T, D, NW, GRAD>;
@@ -318,7 +318,7 @@ struct Engine {
   // one G tile and the A operands of its next logit GEMM in registers. Barriers come only every kK
   // iterations, so the waves of a SIMD drift apart and one wave's vector work overlaps another's MFMAs. A last
   // iteration i = n finishes the pipeline (no loads, no logit GEMM).
-  __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz) {
+  __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz, int* met) {
     const int n = j1 - j0;
     if (n <= 0) return;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // everyone is done with the previous unit's rings
@@ -342,13 +342,13 @@ struct Engine {
       top(0);
       z = logits(aop, own);
       read_a(1, aop);
-      epilogue(0, z, g, bq, e_acc, posz);
+      epilogue(0, z, g, bq, e_acc, posz, met);
       for (int i = 1; i < n; ++i) {
         top(i);
         z = logits(aop, own);
         if (GRAD) grad(i - 1, g, acc);
         read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
-        epilogue(i, z, g, bq, e_acc, posz);
+        epilogue(i, z, g, bq, e_acc, posz, met);
       }
     } else {
       // larger D: the logit GEMM of step i+1 runs in iteration i, reading its A operands from LDS right before
@@ -356,10 +356,10 @@ struct Engine {
       f32x16 za = logits_lds(0, own), zb;
       int i = 0;
       for (; i + 1 < n; i += 2) {
-        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz);
-        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz);
+        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met);
+        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz, met);
       }
-      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz);
+      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met);
     }
     // iteration n: the slot-packed block of step n-1 must have landed
     wait_vm_and_barrier<0>();
@@ -369,11 +369,11 @@ struct Engine {
 
   // Iteration i of the larger-D schedule: Z(i+1) into zn, gradient GEMM of step i-1, epilogue of step i (zc).
   __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GPack<T>& g, f32x16* acc,
-                                  int* bq, float& e_acc, float& posz) {
+                                  int* bq, float& e_acc, float& posz, int* met) {
     top(i);
     if (i + 1 < n_steps()) zn = logits_lds(i + 1, own);
     if (GRAD && i > 0) grad(i - 1, g, acc);
-    epilogue(i, zc, g, bq, e_acc, posz);
+    epilogue(i, zc, g, bq, e_acc, posz, met);
   }
   __device__ inline int n_steps() const { return j1 - j0; }
 
@@ -413,8 +413,10 @@ struct Engine {
   }
 
   // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step from the bucket FIFO,
-  // loss sums (FWD) and the G tile (GRAD).
-  __device__ inline void epilogue(int j, const f32x16& z, GPack<T>& g, int* bq, float& e_acc, float& posz) {
+  // loss sums (FWD), the G tile (GRAD) and, with MET, the Cut Metrics counts of the lane: met[0] logits
+  // predicted positive (z > 0), met[1] positives predicted positive, met[2] positives.
+  __device__ inline void epilogue(int j, const f32x16& z, GPack<T>& g, int* bq, float& e_acc, float& posz,
+                                  int* met) {
     bq[3] = bucket(j + 3);
     const int pb = __builtin_amdgcn_readfirstlane(bq[0]);
     const int pe = __builtin_amdgcn_readfirstlane(bq[1]);
@@ -425,6 +427,10 @@ struct Engine {
       epi_rows<GRAD, false>(z, 0u, c, e_acc, posz);
     else
       epi_items<false>(z, 0u, c);
+    if (MET) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) met[0] += z[i] > 0.f ? 1 : 0;
+    }
     if (pe > pb) {
       const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + j) * 32, FWD, lmask(), lane);
       if (pm) {
@@ -434,6 +440,13 @@ struct Engine {
             if (FWD) posz += z[q];
             c[q] -= 1.f;
           }
+        if (MET) {
+          uint32_t gt = 0u;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) gt |= (z[q] > 0.f ? 1u : 0u) << q;
+          met[1] += __builtin_popcount(pm & gt);
+          met[2] += __builtin_popcount(pm);
+        }
       }
     }
     if (GRAD) g.set(c);
@@ -450,16 +463,17 @@ struct RowsArgs {
   int64_t V, V_pad, n_vs, R_pad;
   float* dhpart;   // [units][RW][D]
   float2* rowpart; // [units][RW]
+  int4* metpart;   // [units][RW]: Cut Metrics counts (predicted positive, true positive, positives)
 };
 
 // ---------------------------------------------------------------------------------------------------------
 // Forward sweep. Persistent: gridDim.x workgroups (a multiple of 8, one per CU); units (split s, row tile t)
 // are assigned in contiguous per-XCD ranges so that the workgroups sharing an L2 stream the same part of E.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool WITH_DH>
+template <typename T, int D, int NW, bool WITH_DH, bool MET>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   using EL = Elem<T>;
-  using EN = Engine<T, D, NW, true, WITH_DH>;
+  using EN = Engine<T, D, NW, true, WITH_DH, MET>;
   constexpr int RW = NW * 32, KS = D / EL::kK, NDB = D / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
@@ -503,14 +517,20 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
 #pragma unroll
     for (int db = 0; db < (WITH_DH ? NDB : 1); ++db) acc[db] = f32x16{};
     float e_acc = 0.f, posz = 0.f;
+    int met[3] = {0, 0, 0};
 
-    en.run(hop, acc, e_acc, posz);
+    en.run(hop, acc, e_acc, posz, met);
 
     // unit results: per-row loss parts and the dH partial of this split
     const int64_t urow = (int64_t)u * RW + wave * 32;  // row of the unit-major partial buffers
     const float e_tot = e_acc + __shfl_xor(e_acc, 32, 64);
     const float p_tot = posz + __shfl_xor(posz, 32, 64);
     if (lane < 32) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    if (MET) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) met[q] += __shfl_xor(met[q], 32, 64);
+      if (lane < 32) a.metpart[urow + lane] = make_int4(met[0], met[1], met[2], 0);
+    }
     if (WITH_DH) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -579,7 +599,7 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
     en.j0 = 0;
     en.j1 = n_st;
     float e_acc = 0.f, posz = 0.f;
-    en.run(eop, acc, e_acc, posz);
+    en.run(eop, acc, e_acc, posz, nullptr);
   }
 
   // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d])
@@ -613,7 +633,7 @@ static int cu_count() {
   return g_cus;
 }
 
-template <typename T, int D, int NW, bool WITH_DH>
+template <typename T, int D, int NW, bool WITH_DH, bool MET>
 static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st) {
   using G = Geo<T, D, NW, WITH_DH>;
   RowsArgs a;
@@ -629,8 +649,9 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   a.R_pad = L.R_pad;
   a.dhpart = (float*)(ws + L.off_dhpart);
   a.rowpart = (float2*)(ws + L.off_rowpart);
+  a.metpart = (int4*)(ws + L.off_metpart);
   const size_t sm = G::kLdsBytes;
-  auto kern = k_rows<T, D, NW, WITH_DH>;
+  auto kern = k_rows<T, D, NW, WITH_DH, MET>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   // persistent: as many workgroups as can be resident at once, a multiple of 8 (one range per XCD)
@@ -687,12 +708,14 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   } while (0)
 
 template <typename T, int D, int NW>
-static hipError_t rows_any(const Layout& L, char* ws, const void* E, bool with_dh, hipStream_t st) {
-  return with_dh ? rows_launch<T, D, NW, true>(L, ws, E, st) : rows_launch<T, D, NW, false>(L, ws, E, st);
+static hipError_t rows_any(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
+  if (met)
+    return with_dh ? rows_launch<T, D, NW, true, true>(L, ws, E, st) : rows_launch<T, D, NW, false, true>(L, ws, E, st);
+  return with_dh ? rows_launch<T, D, NW, true, false>(L, ws, E, st) : rows_launch<T, D, NW, false, false>(L, ws, E, st);
 }
 
-hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, hipStream_t st) {
-  CUTBCE_DISPATCH(L.dtype, rows_any, L, ws, E, with_dh, st);
+hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
+  CUTBCE_DISPATCH(L.dtype, rows_any, L, ws, E, with_dh, met, st);
 }
 
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,

@@ -80,20 +80,22 @@ def dense_to_csr(targets, pad_id: int = -1):
 class Workspace:
     """Reusable explicit-call wrapper: one workspace per problem shape, outputs allocated once."""
 
-    def __init__(self, H, E, item_ids, want_row_loss=False, save_dh=True):
+    def __init__(self, H, E, item_ids, want_row_loss=False, save_dh=True, want_metrics=False):
         self.p = B.problem_of(H, E, item_ids)
         dev = H.device
         self.ws = B.alloc_workspace(self.p, dev)
         self.loss = torch.empty(1, dtype=torch.float32, device=dev)
         self.row_loss = torch.empty(H.shape[0], dtype=torch.float32, device=dev) if want_row_loss else None
         self.dh_saved = torch.empty(H.shape, dtype=torch.float32, device=dev) if save_dh else None
+        # Cut Metrics: TP, FP, FN, TN per row
+        self.metrics = torch.empty(H.shape[0], 4, dtype=torch.int32, device=dev) if want_metrics else None
         self.grad = torch.ones(1, dtype=torch.float32, device=dev)
         self.dH = torch.empty_like(H)
         self.dE = torch.empty_like(E)
 
     def forward(self, H, E, row_offsets, item_ids, row_mask, stream=None):
         B.forward(self.p, H, E, row_offsets, item_ids, row_mask, self.loss, self.row_loss, self.dh_saved, self.ws,
-                  stream)
+                  stream, metrics=self.metrics)
         return self.loss
 
     def backward(self, H, E, row_offsets, item_ids, row_mask, grad=None, want_dH=True, want_dE=True,
