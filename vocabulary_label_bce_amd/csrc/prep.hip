@@ -142,22 +142,31 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
   }
 }
 
-// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order: block = 32 columns x 8 part lanes; part
-// lane y adds parts y, y + 8, y + 16, ... in order, then the 8 lane sums are added in order of y.
-__global__ void __launch_bounds__(256) k_sum_parts(const double* __restrict__ part, int64_t nparts, int D,
-                                                   double* __restrict__ out) {
-  __shared__ double sh[8][32];
+// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order: block = 32 columns x 32 part lanes; part
+// lane y adds parts y + 32 m for m = 0, 1, ... into four running sums (m mod 4, so four loads are in flight),
+// adds those four, then the 32 lane sums are added in order of y.
+__global__ void __launch_bounds__(1024) k_sum_parts(const double* __restrict__ part, int64_t nparts, int D,
+                                                    double* __restrict__ out) {
+  __shared__ double sh[32][33];
   const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
   const int d = blockIdx.x * 32 + tx;
-  double s = 0.0;
-  if (d < D)
-    for (int64_t p = ty; p < nparts; p += 8) s += part[p * D + d];
-  sh[ty][tx] = s;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  if (d < D) {
+    int64_t p = ty;
+    for (; p + 96 < nparts; p += 128) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += part[(p + 32 * q) * D + d];
+    }
+    // at most three parts are left
+    if (p < nparts) s[0] += part[p * D + d];
+    if (p + 32 < nparts) s[1] += part[(p + 32) * D + d];
+    if (p + 64 < nparts) s[2] += part[(p + 64) * D + d];
+  }
+  sh[ty][tx] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
   if (ty == 0 && d < D) {
     double t = 0.0;
-#pragma unroll
-    for (int y = 0; y < 8; ++y) t += sh[y][tx];
+    for (int y = 0; y < 32; ++y) t += sh[y][tx];
     out[d] = t;
   }
 }
@@ -176,7 +185,7 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
                      (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
   return hipGetLastError();
 }
@@ -235,7 +244,7 @@ hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
                      (const double*)(ws + L.off_sumE_part), L.n_eblk, L.D, (double*)(ws + L.off_sumE));
   return hipGetLastError();
 }
