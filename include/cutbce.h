@@ -20,8 +20,10 @@
  *     allocates device memory and keeps no state between calls (apart from the opt-in timing records of
  *     cutbce_profile_enable).
  *   - H [R][D], E [V][D], dH [R][D], dE [V][D] are dense row-major, in the problem's element type, 16-byte
- *     aligned. row_offsets int32 [R+1] (row_offsets[0] = 0, non-decreasing, row_offsets[R] = nnz); item_ids
- *     int32 [nnz], any order within a row, repeats allowed; row_mask uint8 [R] (0 = padding, else valid).
+ *     aligned. row_offsets int32 [R+1] (row_offsets[0] = 0, non-decreasing, row_offsets[R] <= nnz); item_ids
+ *     int32 [nnz], any order within a row, repeats allowed, entries from row_offsets[R] on unused (so a
+ *     capacity-sized buffer from cutbce_targets_to_csr can be passed as is); row_mask uint8 [R]
+ *     (0 = padding, else valid).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs asynchronously; no call
  *     synchronises with the host. Scalars that the device produces or consumes (loss, grad_loss) stay in
  *     device memory.
@@ -103,10 +105,23 @@ cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device-side check of the targets: writes to *bad (device int32) the number of ids outside [0, V) plus
- * the number of rows whose offsets decrease, plus 1 if row_offsets[0] != 0 or row_offsets[R] != nnz.
+ * the number of rows whose offsets decrease, plus 1 if row_offsets[0] != 0 or row_offsets[R] > nnz (ids are
+ * checked up to min(row_offsets[R], nnz)).
  * 0 means the targets are well formed. Needs no workspace. */
 cutbce_status cutbce_validate_targets(const cutbce_problem *p, const int32_t *row_offsets,
                                       const int32_t *item_ids, int32_t *bad, void *stream);
+
+/* Dense padded targets -> CSR positives (the [B, N, L] target slots of the paper's Listing 1).
+ *   rows        R = B*N rows; slots L >= 0 id slots per row.
+ *   targets     (device) int32 [R][L], row-major; a slot equal to pad_id is padding and is dropped.
+ *   row_offsets (device) int32 [R+1], written: row_offsets[0] = 0, row_offsets[r+1] - row_offsets[r] = kept
+ *               slots of row r; row_offsets[R] = nnz, the number of kept slots.
+ *   item_ids    (device) int32 [R*L] (capacity), written: the kept ids of each row in slot order, rows in order;
+ *               entries from nnz on are left untouched. Repeated ids are kept (the loss counts them once).
+ * Errors: SHAPE when R < 1, L < 0 or R*L >= 2^31; NULL for a missing pointer; ALIGN for a pointer that is not
+ * 4-byte aligned. Needs no workspace; asynchronous on `stream`. */
+cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t *targets, int32_t pad_id,
+                                    int32_t *row_offsets, int32_t *item_ids, void *stream);
 
 /* Opt-in kernel timing for benchmarks (host calls). While enabled, every launch of the two logit-tile sweeps
  * (kind 0: forward rows sweep, kind 1: backward dE sweep) is bracketed by HIP events recorded on the launch

@@ -165,3 +165,18 @@ def metrics(H, E, row_offsets, item_ids, row_mask, rows=None, eps: float = 0.0, 
                                      n, rp, _ptr(out))
     _check(st)
     return out
+
+
+def targets_to_csr(targets, pad_id: int = -1):
+    """Dense padded targets [..., L] -> (row_offsets int32 [R+1], item_ids int32 [nnz]): the definition written
+    out (the [B, N, L] target slots of the paper's Listing 1; a slot equal to pad_id is padding). Row r keeps
+    its non-pad slots in slot order; rows follow in order."""
+    t = np.asarray(targets.cpu().numpy() if hasattr(targets, "cpu") else targets)
+    t = t.reshape(int(np.prod(t.shape[:-1])), t.shape[-1]) if t.ndim >= 2 else t.reshape(1, -1)
+    offsets = [0]
+    ids = []
+    for row in t:
+        kept = [int(x) for x in row if int(x) != pad_id]
+        ids.extend(kept)
+        offsets.append(offsets[-1] + len(kept))
+    return np.asarray(offsets, np.int32), np.asarray(ids, np.int32)

@@ -106,6 +106,17 @@ def test_backward_and_validate_reject_bad_arguments():
     assert lib.cutbce_workspace_size(ctypes.byref(p), None) == 1
 
 
+def test_targets_to_csr_rejects_bad_arguments():
+    lib = B.lib()
+    vp = ctypes.c_void_p
+    assert lib.cutbce_targets_to_csr(0, 4, vp(FAKE), -1, vp(FAKE), vp(FAKE), None) == 2  # no rows
+    assert lib.cutbce_targets_to_csr(8, -1, vp(FAKE), -1, vp(FAKE), vp(FAKE), None) == 2  # negative slots
+    assert lib.cutbce_targets_to_csr(1 << 20, 1 << 12, vp(FAKE), -1, vp(FAKE), vp(FAKE), None) == 2  # R*L >= 2^31
+    assert lib.cutbce_targets_to_csr(8, 4, None, -1, vp(FAKE), vp(FAKE), None) == 1
+    assert lib.cutbce_targets_to_csr(8, 4, vp(FAKE), -1, None, vp(FAKE), None) == 1
+    assert lib.cutbce_targets_to_csr(8, 4, vp(FAKE + 2), -1, vp(FAKE), vp(FAKE), None) == 4
+
+
 def test_library_source_never_allocates_device_memory():
     csrc = os.path.join(ROOT, "vocabulary_label_bce_amd", "csrc")
     for f in os.listdir(csrc):

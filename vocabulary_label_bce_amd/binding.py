@@ -31,6 +31,7 @@ class Problem(ctypes.Structure):
 
 
 EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
+           "cutbce_targets_to_csr",
            "cutbce_profile_enable", "cutbce_profile_read", "cutbce_status_string", "cutbce_version"]
 
 
@@ -49,6 +50,7 @@ def lib():
         L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
+        L.cutbce_targets_to_csr.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp]
         L.cutbce_profile_enable.argtypes = [i32]
         L.cutbce_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
         L.cutbce_profile_enable.restype = i32
@@ -56,7 +58,8 @@ def lib():
         L.cutbce_status_string.argtypes = [i32]
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
-        for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets"):
+        for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
+                  "cutbce_targets_to_csr"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -111,6 +114,13 @@ def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_sa
     _check(lib().cutbce_backward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
                                  _ptr(row_mask), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH), _ptr(dE), _ptr(ws),
                                  ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def targets_to_csr(targets, pad_id: int, row_offsets, item_ids, stream=None):
+    """cutbce_targets_to_csr: targets int32 [R, L] on the device -> row_offsets [R+1], item_ids [R*L] (in place)."""
+    R, L = targets.shape
+    _check(lib().cutbce_targets_to_csr(int(R), int(L), _ptr(targets), int(pad_id), _ptr(row_offsets),
+                                       _ptr(item_ids), _stream(stream)))
 
 
 def validate_targets(p: Problem, row_offsets, item_ids, bad, stream=None):

@@ -160,7 +160,7 @@ cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E
 
 extern "C" {
 
-int cutbce_version(void) { return 101; }
+int cutbce_version(void) { return 102; }
 
 const char* cutbce_status_string(cutbce_status s) {
   switch (s) {
@@ -247,6 +247,15 @@ cutbce_status cutbce_validate_targets(const cutbce_problem* p, const int32_t* ro
   if (!row_offsets || !bad || (p->nnz > 0 && !item_ids)) return CUTBCE_ERR_NULL;
   if (misaligned(row_offsets, 4) || misaligned(item_ids, 4) || misaligned(bad, 4)) return CUTBCE_ERR_ALIGN;
   return hip_status(launch_validate(p->rows, p->vocab, p->nnz, row_offsets, item_ids, bad, (hipStream_t)stream));
+}
+
+cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t* targets, int32_t pad_id,
+                                    int32_t* row_offsets, int32_t* item_ids, void* stream) {
+  if (rows < 1 || slots < 0 || rows > (int64_t)0x7fffffff - 1024 || rows * (int64_t)slots > 0x7fffffffLL)
+    return CUTBCE_ERR_SHAPE;
+  if (!row_offsets || (slots > 0 && (!targets || !item_ids))) return CUTBCE_ERR_NULL;
+  if (misaligned(targets, 4) || misaligned(row_offsets, 4) || misaligned(item_ids, 4)) return CUTBCE_ERR_ALIGN;
+  return hip_status(launch_targets_to_csr(rows, slots, targets, pad_id, row_offsets, item_ids, (hipStream_t)stream));
 }
 
 cutbce_status cutbce_profile_enable(int on) {

@@ -111,6 +111,8 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                               hipStream_t st);
 hipError_t launch_scale_dh(const Layout& L, const float* src, const float* grad_loss, void* dH, hipStream_t st);
+hipError_t launch_targets_to_csr(int64_t R, int L, const int32_t* targets, int32_t pad, int32_t* row_offsets,
+                                 int32_t* item_ids, hipStream_t st);
 hipError_t launch_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* row_offsets,
                            const int32_t* item_ids, int32_t* bad, hipStream_t st);
 

@@ -397,6 +397,59 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// Dense padded targets -> CSR ("Cut Binary Cross Entropy", Listing 1 takes targets as [B, N, L] id slots).
+// Row r's ids are targets[r][0..L) in slot order with every slot equal to pad_id dropped.
+//   count  : row_offsets[r + 1] = number of kept slots of row r; row_offsets[0] = 0
+//   scan   : one workgroup turns row_offsets[1..R] into inclusive prefix sums, 1024 rows at a time
+//   scatter: row r writes its kept ids, in slot order, to item_ids[row_offsets[r]...]
+// ---------------------------------------------------------------------------------------------------------
+__global__ void k_t2c_count(const int32_t* __restrict__ targets, int64_t R, int L, int32_t pad,
+                            int32_t* __restrict__ row_offsets) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r == 0) row_offsets[0] = 0;
+  if (r >= R) return;
+  int n = 0;
+  for (int k = 0; k < L; ++k) n += targets[r * L + k] != pad ? 1 : 0;
+  row_offsets[r + 1] = n;
+}
+
+__global__ void __launch_bounds__(1024) k_t2c_scan(int32_t* __restrict__ x, int64_t n) {
+  __shared__ int sh[16];
+  int base = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+    const int64_t i = c0 + threadIdx.x;
+    const int v = i < n ? x[i] : 0;
+    int tot;
+    const int ex = block_excl_scan(v, sh, tot);
+    if (i < n) x[i] = base + ex + v;
+    base += tot;
+  }
+}
+
+__global__ void k_t2c_scatter(const int32_t* __restrict__ targets, int64_t R, int L, int32_t pad,
+                              const int32_t* __restrict__ row_offsets, int32_t* __restrict__ item_ids) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  int o = row_offsets[r];
+  for (int k = 0; k < L; ++k) {
+    const int32_t v = targets[r * L + k];
+    if (v != pad) item_ids[o++] = v;
+  }
+}
+
+hipError_t launch_targets_to_csr(int64_t R, int L, const int32_t* targets, int32_t pad, int32_t* row_offsets,
+                                 int32_t* item_ids, hipStream_t st) {
+  const unsigned blocks = (unsigned)((R + 255) / 256);
+  hipLaunchKernelGGL(k_t2c_count, dim3(blocks), dim3(256), 0, st, targets, R, L, pad, row_offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_t2c_scan, dim3(1), dim3(1024), 0, st, row_offsets + 1, R);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_t2c_scatter, dim3(blocks), dim3(256), 0, st, targets, R, L, pad, row_offsets, item_ids);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // Target validation.
 // ---------------------------------------------------------------------------------------------------------
 __global__ void k_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* __restrict__ ro,
@@ -406,9 +459,10 @@ __global__ void k_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* __r
   const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   for (int64_t r = t0; r < R; r += stride)
     if (ro[r + 1] < ro[r]) ++nb;
-  for (int64_t p = t0; p < nnz; p += stride)
+  const int64_t used = ro[R] < nnz ? (ro[R] > 0 ? ro[R] : 0) : nnz;  // ids past row_offsets[R] are unused
+  for (int64_t p = t0; p < used; p += stride)
     if (ids[p] < 0 || ids[p] >= V) ++nb;
-  if (t0 == 0 && (ro[0] != 0 || ro[R] != nnz)) ++nb;
+  if (t0 == 0 && (ro[0] != 0 || ro[R] > nnz)) ++nb;
   if (nb) atomicAdd(bad, nb);
 }
 

@@ -68,13 +68,41 @@ def cut_bce(H, E, row_offsets, item_ids, row_mask):
 
 
 def dense_to_csr(targets, pad_id: int = -1):
-    """Targets as a padded [B, N, L] (or [R, L]) id tensor -> (row_offsets, item_ids), dropping `pad_id`."""
-    t = targets.reshape(-1, targets.shape[-1])
-    keep = t != pad_id
-    counts = keep.sum(1)
-    row_offsets = torch.zeros(t.shape[0] + 1, dtype=torch.int32, device=t.device)
-    row_offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
-    return row_offsets, t[keep].to(torch.int32)
+    """Padded targets [B, N, L] (or [R, L]) on the GPU -> (row_offsets [R+1], item_ids [R*L]) on the device
+    (cutbce_targets_to_csr): slots equal to `pad_id` are dropped, order is kept; item_ids is capacity-sized and
+    only its first row_offsets[R] entries are used. No host synchronisation."""
+    if not targets.is_cuda:
+        raise ValueError("dense_to_csr runs on the GPU only")
+    rows = 1
+    for n in targets.shape[:-1]:
+        rows *= int(n)
+    t = targets.reshape(rows, targets.shape[-1]).to(torch.int32).contiguous()
+    R, L = t.shape
+    row_offsets = torch.empty(R + 1, dtype=torch.int32, device=t.device)
+    item_ids = torch.empty(max(R * L, 1), dtype=torch.int32, device=t.device)
+    B.targets_to_csr(t, pad_id, row_offsets, item_ids)
+    return row_offsets, item_ids
+
+
+def cut_binary_cross_entropy(activations, embeddings, targets, weights=None, pad_id: int = -1):
+    """The paper's Listing 1 call shape: activations [B, N, D], embeddings [V, D], targets [B, N, L] (ids, slots
+    equal to `pad_id` are padding), weights [B, N] per position or None (all positions train).
+
+    The weights are read as a 0/1 mask: a position with weight 0 is padding and is left out of the average,
+    every other position is trained. Weights other than 0 and 1 raise (checking them reads the tensor back).
+    Returns the scalar loss; gradients flow to activations and embeddings.
+    """
+    B_, N = activations.shape[0], activations.shape[1]
+    H = activations.reshape(B_ * N, activations.shape[-1])
+    row_offsets, item_ids = dense_to_csr(targets, pad_id)
+    if weights is None:
+        mask = torch.ones(B_ * N, dtype=torch.uint8, device=H.device)
+    else:
+        w = weights.reshape(B_ * N)
+        if w.dtype.is_floating_point and not bool(((w == 0) | (w == 1)).all()):
+            raise ValueError("weights other than 0 and 1 are not supported: a weight marks a position as trained")
+        mask = (w != 0).to(torch.uint8)
+    return cut_bce(H, embeddings, row_offsets, item_ids, mask)
 
 
 class Workspace:
