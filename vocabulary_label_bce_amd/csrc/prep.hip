@@ -29,45 +29,67 @@ static hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Exclusive scan of one int per thread over a 1024-thread workgroup; `total` gets the workgroup sum.
+__device__ inline int block_excl_scan(int v, int* sh, int& total) {
+  // 1024 threads: wave inclusive scan with shuffles, then wave totals through LDS
+  const int lane = lane_id(), wave = threadIdx.x / 64;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) off += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  total = tot;
+  return off + x - v;
+}
+
 // ---------------------------------------------------------------------------------------------------------
-// Row compaction: one workgroup walks the mask in chunks of 1024 rows, keeping ascending order.
+// Row compaction: one workgroup walks the mask in chunks of 4096 rows (4 consecutive rows per thread), keeping
+// ascending order.
 // ---------------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask,
                                                   const int32_t* __restrict__ row_offsets, int64_t R,
                                                   int64_t R_pad, int64_t V, Ctl* ctl, int32_t* row_of,
                                                   int32_t* compact_of, int2* rptr) {
-  __shared__ int wsum[16];
-  __shared__ int base_s;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-  if (tid == 0) base_s = 0;
-  __syncthreads();
-  for (int64_t c0 = 0; c0 < R; c0 += 1024) {
-    const int64_t r = c0 + tid;
-    const bool f = r < R && mask[r] != 0;
-    const uint64_t b = __ballot(f);
-    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
-    if (lane == 0) wsum[wave] = __popcll(b);
-    __syncthreads();
-    int off = base_s, tot = 0;
-    for (int w = 0; w < 16; ++w) {
-      if (w < wave) off += wsum[w];
-      tot += wsum[w];
+  __shared__ int sh[16];
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int64_t c0 = 0; c0 < R; c0 += 4096) {
+    const int64_t r0 = c0 + 4 * tid;
+    bool f[4];
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = r0 + j < R && mask[r0 + j] != 0;
+      n += f[j] ? 1 : 0;
     }
-    if (r < R) {
-      if (f) {
-        const int k = off + pre;
-        row_of[k] = (int32_t)r;
-        compact_of[r] = k;
-        rptr[k] = make_int2(row_offsets[r], row_offsets[r + 1]);
-      } else {
-        compact_of[r] = -1;
+    int tot;
+    int k = base + block_excl_scan(n, sh, tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t r = r0 + j;
+      if (r < R) {
+        if (f[j]) {
+          row_of[k] = (int32_t)r;
+          compact_of[r] = k;
+          rptr[k] = make_int2(row_offsets[r], row_offsets[r + 1]);
+          ++k;
+        } else {
+          compact_of[r] = -1;
+        }
       }
     }
-    __syncthreads();
-    if (tid == 0) base_s += tot;
-    __syncthreads();
+    base += tot;
   }
-  const int nv = base_s;
+  const int nv = base;
   for (int64_t k = nv + tid; k < R_pad; k += 1024) {
     row_of[k] = -1;
     rptr[k] = make_int2(0, 0);
@@ -252,27 +274,6 @@ hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp
 // ---------------------------------------------------------------------------------------------------------
 // Multi-block exclusive scan of int32 counts, in place: x[i] <- sum_{j<i} x[j] for i <= n (x[n] = total).
 // ---------------------------------------------------------------------------------------------------------
-__device__ inline int block_excl_scan(int v, int* sh, int& total) {
-  // 1024 threads: wave inclusive scan with shuffles, then wave totals through LDS
-  const int lane = lane_id(), wave = threadIdx.x / 64;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  int off = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) off += sh[w];
-    tot += sh[w];
-  }
-  __syncthreads();
-  total = tot;
-  return off + x - v;
-}
-
 constexpr int kScanPerThread = kScanBlock / 1024;
 
 __global__ void __launch_bounds__(1024) k_scan_sums(const int32_t* __restrict__ x, int64_t n,
@@ -346,12 +347,13 @@ __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, con
                                                 const int32_t* __restrict__ ids, int64_t V, bool rows_side,
                                                 int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
                                                 int2* __restrict__ pairs, int* bad) {
-  const int64_t k = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  const int lane = lane_id();
+  // 8 lanes per compact row (rows hold a handful of ids in the usual workloads)
+  const int64_t k = (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8;
+  const int sub = threadIdx.x % 8;
   if (k >= ctl->n_valid) return;
   const int2 rp = rptr[k];
   int nbad = 0;
-  for (int p = rp.x + lane; p < rp.y; p += 64) {
+  for (int p = rp.x + sub; p < rp.y; p += 8) {
     const int v = ids[p];
     if (v < 0 || v >= V) {
       ++nbad;
@@ -378,7 +380,7 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   const int64_t minor = rows_side ? L.n_vs : L.n_rs;
   hipError_t e = fill_i32(bptr, nb + 1, 0, st);
   if (e != hipSuccess) return e;
-  const int64_t blocks = L.R_pad / 4;
+  const int64_t blocks = L.R_pad / 32;  // 32 rows of 8 lanes per 256-thread block
   if (L.nnz > 0) {
     hipLaunchKernelGGL(k_bucket<false>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
                        (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bptr,

@@ -8,8 +8,8 @@
 
 `traffic` reads one FETCH_SIZE pass and one WRITE_SIZE pass (KiB per dispatch). It scales each counter by
 what the same counter read for a plain copy kernel that moved a known number of bytes in the same run, so the
-result is in HBM bytes per launch. The JSON records a digest of the kernel sources, and a reader treats the
-figure as stale once the sources differ.
+result is in HBM bytes per launch. The JSON records a digest of the sources that define the two sweep kernels
+(sweep.hip and the shared layouts in common.h), and a reader treats the figure as stale once they differ.
 """
 from __future__ import annotations
 
@@ -24,14 +24,16 @@ import statistics
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+SWEEP_SOURCES = ("common.h", "sweep.hip")
+
+
 def source_digest() -> str:
-    """sha256 over the library's kernel sources (file names and contents, sorted)."""
+    """sha256 over the sources of the sweep kernels (file names and contents)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in SWEEP_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
