@@ -119,6 +119,14 @@ def test_all_rows_masked_and_rows_without_positives():
     assert got["loss"] == 0.0 and not got["dH"].any() and not got["dE"].any() and not got["row_loss"].any()
 
 
+@pytest.mark.parametrize("R,V,dtype", [(1, 1, "bf16"), (1, 1, "f32"), (1, 33, "bf16"), (2, 257, "f32"),
+                                       (33, 1, "bf16")])
+def test_smallest_shapes(R, V, dtype):
+    p = W.custom_problem(R, V, 64, dtype=dtype, seed=R * 1000 + V, h_std=0.8, e_std=0.8, pos_per_row=(1, 1))
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=1.0)
+    _check(p, _run(p, g=1.0), ref, excess=False)
+
+
 def test_deterministic_and_recompute_path_matches():
     p = W.custom_problem(300, 5000, 128, dtype="bf16", seed=14, h_std=0.3, e_std=0.3, pos_per_row=(1, 8),
                          mask_frac=0.3)
