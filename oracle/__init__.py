@@ -5,8 +5,8 @@ It shares no code with the GPU library (``vocabulary_label_bce_amd``) and never 
 
 The arithmetic lives in ``cutbce_oracle.c`` (plain C, float64, OpenMP over rows/items); this module only
 compiles it with gcc and marshals arrays. See the header of the C file for the equations it follows
-("Cut Binary Cross Entropy", Section III-A Eq. (1)-(3), Section III-B Eq. (4) and the Cut Metrics of
-Section III-D).
+("Cut Binary Cross Entropy", Section III-A Eq. (1)-(3), Section III-B Eq. (4), the Cut Metrics of
+Section III-D and the full-vocabulary top-k / Hit@k evaluation of Section I-E).
 """
 from __future__ import annotations
 
@@ -54,7 +54,9 @@ def _load(plant: int = 0):
         lib.oracle_items.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
         lib.oracle_full.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp, vp]
         lib.oracle_metrics.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
-        for f in (lib.oracle_rows, lib.oracle_items, lib.oracle_full, lib.oracle_metrics, lib.oracle_num_threads):
+        lib.oracle_topk.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
+        for f in (lib.oracle_rows, lib.oracle_items, lib.oracle_full, lib.oracle_metrics, lib.oracle_topk,
+                  lib.oracle_num_threads):
             f.restype = ctypes.c_int
         _libs[plant] = lib
         return lib
@@ -165,6 +167,25 @@ def metrics(H, E, row_offsets, item_ids, row_mask, rows=None, eps: float = 0.0, 
                                      n, rp, _ptr(out))
     _check(st)
     return out
+
+
+def topk(H, E, row_offsets, item_ids, row_mask, k: int, rows=None, plant: int = 0):
+    """Full-vocabulary top-k per row (all rows when `rows` is None): dict(ids int64 [n, k], vals float64 [n, k],
+    hits int64 [n]) -- the k largest logits, ties by smaller item id; hits = how many of them are positives.
+    Masked rows: ids -1, vals -inf, hits 0."""
+    h, e, dt, R, V, D, ro, ids, m = _prep(H, E, row_offsets, item_ids, row_mask)
+    if rows is None:
+        n, rp = R, None
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n, rp = rr.size, _ptr(rr)
+    oid = np.zeros((n, k), np.int64)
+    oval = np.zeros((n, k), np.float64)
+    hits = np.zeros(n, np.int64)
+    st = _load(plant).oracle_topk(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m), int(k), n, rp,
+                                  _ptr(oid), _ptr(oval), _ptr(hits))
+    _check(st)
+    return dict(ids=oid, vals=oval, hits=hits)
 
 
 def targets_to_csr(targets, pad_id: int = -1):

@@ -25,6 +25,10 @@
  *   - R_v = 0 (every row masked) gives loss 0 and zero gradients;
  *   - row_loss[r] is the unnormalised sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
  *
+ * Full-vocabulary top-k (Section I-E evaluation): per valid row, the k items with the largest logits, ordered
+ * by logit (descending) and, among equal logits, by item id (ascending); Hit@k counts a row as a hit when at
+ * least one of its positives is among them.
+ *
  * Cut Metrics (Section III-D): per position, the confusion counts TP, FP, FN, TN over the V items, computed
  * from the same logits without materialising them. The section names no threshold; the plain reading used
  * here is "predict positive iff sigma(z) > 1/2", i.e. iff z > 0 (z = 0 is a negative prediction). Masked rows
@@ -327,6 +331,79 @@ int oracle_metrics(int64_t R, int64_t V, int D, int dtype, const void *H, const 
                 if (fabs(z) <= eps) ++o[4];
             }
             mark_row(row_offsets, item_ids, r, ymap, 0);
+        }
+        free(ymap);
+    }
+    return err;
+}
+
+/* Does (za, va) rank before (zb, vb): larger logit first, smaller item id among equal logits. */
+static int ranks_before(double za, int64_t va, double zb, int64_t vb) {
+#if ORACLE_PLANT == 7
+    return za > zb || (za == zb && va > vb); /* planted: ties broken towards the larger id */
+#else
+    return za > zb || (za == zb && va < vb);
+#endif
+}
+
+/*
+ * Full-vocabulary top-k for each requested row (all R when rows == NULL): ids[i][0..k) and vals[i][0..k) hold
+ * the k best items of row r in rank order (see ranks_before) and their float64 logits; hits[i] (when hits !=
+ * NULL) counts how many of them are among the row's positives. Masked rows get ids -1, vals -inf, hits 0.
+ * Requires 1 <= k <= V.
+ */
+int oracle_topk(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
+                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, int k,
+                int64_t n_rows, const int64_t *rows, int64_t *ids, double *vals, int64_t *hits) {
+    int64_t rv;
+    int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
+    if (st) return st;
+    if (k < 1 || k > V) return OR_BAD_SHAPE;
+    if (!rows) n_rows = R;
+    int err = 0;
+#pragma omp parallel
+    {
+        uint8_t *ymap = (uint8_t *)calloc((size_t)V, 1);
+        if (!ymap) {
+#pragma omp atomic write
+            err = OR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            if (!ymap) continue;
+            int64_t r = rows ? rows[i] : i;
+            int64_t *id = ids + (size_t)i * k;
+            double *va = vals + (size_t)i * k;
+            for (int q = 0; q < k; ++q) {
+                id[q] = -1;
+                va[q] = -INFINITY;
+            }
+            if (hits) hits[i] = 0;
+            if (r < 0 || r >= R) {
+#pragma omp atomic write
+                err = OR_BAD_SHAPE;
+                continue;
+            }
+            if (!row_mask[r]) continue;
+            /* insertion into a sorted list of the k best so far */
+            int64_t filled = 0;
+            for (int64_t v = 0; v < V; ++v) {
+                double z = dot_rv(H, E, dtype, r, v, D);
+                if (filled == k && !ranks_before(z, v, va[k - 1], id[k - 1])) continue;
+                int64_t q = filled < k ? filled++ : k - 1;
+                while (q > 0 && ranks_before(z, v, va[q - 1], id[q - 1])) {
+                    va[q] = va[q - 1];
+                    id[q] = id[q - 1];
+                    --q;
+                }
+                va[q] = z;
+                id[q] = v;
+            }
+            if (hits) {
+                mark_row(row_offsets, item_ids, r, ymap, 1);
+                for (int q = 0; q < k; ++q) hits[i] += ymap[id[q]] ? 1 : 0;
+                mark_row(row_offsets, item_ids, r, ymap, 0);
+            }
         }
         free(ymap);
     }
