@@ -111,6 +111,20 @@ cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void
 cutbce_status cutbce_validate_targets(const cutbce_problem *p, const int32_t *row_offsets,
                                       const int32_t *item_ids, int32_t *bad, void *stream);
 
+/* Full-vocabulary top-k scoring (the evaluation of Section I-E: hidden states projected onto every item, items
+ * ranked, Hit@k). For each valid row r, the k items with the largest logits z_rv = H[r] . E[v], ranked by logit
+ * (descending) and, among equal logits, by item id (ascending); the logits are never written to memory.
+ *   k          1 <= k <= 8 and k <= V.
+ *   top_vals   (device) float [R][k], written: the float32 logits of the ranked items; -inf for masked rows.
+ *   top_ids    (device) int32 [R][k], written: the ranked item ids; -1 for masked rows.
+ *   hits       (device) int32 [R] or NULL: how many of the row's k items are among its positives (row_offsets /
+ *              item_ids as in cutbce_forward; a repeated id counts once). Hit@k of a set of rows is the fraction
+ *              with hits > 0. 0 for masked rows.
+ * Uses the same workspace as cutbce_forward. Errors as for cutbce_forward; SHAPE for k out of range. */
+cutbce_status cutbce_topk(const cutbce_problem *p, const void *H, const void *E, const int32_t *row_offsets,
+                          const int32_t *item_ids, const uint8_t *row_mask, int32_t k, float *top_vals,
+                          int32_t *top_ids, int32_t *hits, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Dense padded targets -> CSR positives (the [B, N, L] target slots of the paper's Listing 1).
  *   rows        R = B*N rows; slots L >= 0 id slots per row.
  *   targets     (device) int32 [R][L], row-major; a slot equal to pad_id is padding and is dropped.

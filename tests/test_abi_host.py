@@ -106,6 +106,23 @@ def test_backward_and_validate_reject_bad_arguments():
     assert lib.cutbce_workspace_size(ctypes.byref(p), None) == 1
 
 
+def test_topk_rejects_bad_arguments():
+    lib = B.lib()
+    vp = ctypes.c_void_p
+    p = B.problem(64, 4096, 100, 128, B.BF16)
+    ws = B.workspace_size(p)
+    args = lambda k, vals=FAKE, ids=FAKE: (ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), k,
+                                           vp(vals) if vals else None, vp(ids) if ids else None, None, vp(FAKE), ws,
+                                           None)
+    assert lib.cutbce_topk(*args(0)) == 2
+    assert lib.cutbce_topk(*args(9)) == 2
+    assert lib.cutbce_topk(*args(8, vals=0)) == 1
+    assert lib.cutbce_topk(*args(8, ids=FAKE + 2)) == 4
+    small = B.problem(64, 5, 100, 128, B.BF16)
+    assert lib.cutbce_topk(ctypes.byref(small), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 6, vp(FAKE),
+                           vp(FAKE), None, vp(FAKE), B.workspace_size(small), None) == 2  # k > V
+
+
 def test_targets_to_csr_rejects_bad_arguments():
     lib = B.lib()
     vp = ctypes.c_void_p

@@ -1,0 +1,103 @@
+"""GPU full-vocabulary top-k and Hit@k ("Cut Binary Cross Entropy", Section I-E evaluation) through the C ABI,
+against the float64 oracle.
+
+The GPU ranks float32 logits; two items whose float64 logits differ by less than the float32 dot-product error
+bound eps = (D + 2) 2^-24 |H_r| max_v |E_v| (doubled) may legitimately swap. So, per valid row: the returned ids
+are distinct real items; their returned logits equal the exact ones within eps and do not increase; every
+returned item's exact logit is at least the oracle's k-th best minus 2 eps; the returned logits match the
+oracle's k best within 2 eps; equal returned logits come in ascending id order; hits equals the number of
+returned ids among the row's positives. Masked rows return -1 / -inf / 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vocabulary_label_bce_amd import workloads as W
+from vocabulary_label_bce_amd.ops import topk
+
+pytestmark = pytest.mark.gpu
+
+
+def _eps(H, E):
+    D = H.shape[1]
+    return 2.0 * (D + 2) * 2.0 ** -24 * np.linalg.norm(H, axis=1) * np.linalg.norm(E, axis=1).max()
+
+
+def _check(p, k, vals, ids, hits, rows=None):
+    H = p["H"].double().numpy()
+    E = p["E"].double().numpy()
+    V = E.shape[0]
+    m = p["row_mask"].numpy()
+    rows = np.arange(H.shape[0]) if rows is None else np.asarray(rows)
+    ref = oracle.topk(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], k, rows=rows)
+    eps = _eps(H[rows], E)
+    ro = p["row_offsets"].numpy()
+    pos = p["item_ids"].numpy()
+    for n, r in enumerate(rows):
+        if not m[r]:
+            assert (ids[r] == -1).all() and np.isneginf(vals[r]).all() and hits[r] == 0
+            continue
+        g_ids = ids[r].astype(np.int64)
+        assert len(set(g_ids.tolist())) == k and (g_ids >= 0).all() and (g_ids < V).all()
+        z = H[r] @ E[g_ids].T
+        assert np.abs(vals[r] - z).max() <= eps[n], (r, np.abs(vals[r] - z).max(), eps[n])
+        assert (np.diff(vals[r]) <= 0).all()
+        assert (z >= ref["vals"][n, k - 1] - 2 * eps[n]).all()
+        assert np.abs(vals[r] - ref["vals"][n]).max() <= 2 * eps[n]
+        for q in range(k - 1):
+            if vals[r][q] == vals[r][q + 1]:
+                assert g_ids[q] < g_ids[q + 1]
+        assert hits[r] == len(set(g_ids.tolist()) & set(pos[ro[r]:ro[r + 1]].tolist()))
+
+
+CASES = [
+    ("bf16_d64", dict(R=200, V=3000, D=64, dtype="bf16", seed=51, h_std=0.5, e_std=0.5, pos_per_row=(1, 8),
+                      mask_frac=0.1), 8),
+    ("bf16_d128_k1", dict(R=63, V=4097, D=128, dtype="bf16", seed=52, h_std=0.3, e_std=0.3, pos_per_row=(0, 6)), 1),
+    ("bf16_d256_k5", dict(R=90, V=777, D=256, dtype="bf16", seed=53, h_std=0.2, e_std=0.2, pos_per_row=(1, 8),
+                          mask_frac=0.2), 5),
+    ("bf16_d512", dict(R=40, V=555, D=512, dtype="bf16", seed=54, h_std=0.1, e_std=0.2, pos_per_row=(1, 30)), 8),
+    ("f32_d64", dict(R=257, V=513, D=64, dtype="f32", seed=55, h_std=0.3, e_std=0.3, pos_per_row=(1, 8)), 8),
+    ("f32_d128_k3", dict(R=100, V=700, D=128, dtype="f32", seed=56, h_std=0.3, e_std=0.3, pos_per_row=(1, 8)), 3),
+    ("bf16_small_V", dict(R=30, V=9, D=64, dtype="bf16", seed=57, h_std=0.5, e_std=0.5, pos_per_row=(1, 3)), 8),
+]
+
+
+@pytest.mark.parametrize("name,kw,k", CASES, ids=[c[0] for c in CASES])
+def test_topk_matches_oracle(name, kw, k):
+    p = W.custom_problem(**kw)
+    E = p["E"].clone()
+    E[7 % kw["V"]] = E[3 % kw["V"]]  # identical embeddings: equal logits in every row (tie rule)
+    p["E"] = E
+    d = {key: v.cuda() for key, v in p.items()}
+    vals, ids, hits = topk(d["H"], d["E"], k, d["row_offsets"], d["item_ids"], d["row_mask"])
+    torch.cuda.synchronize()
+    _check(p, k, vals.cpu().numpy(), ids.cpu().numpy(), hits.cpu().numpy())
+
+
+def test_topk_ties_pick_smaller_ids():
+    p = W.custom_problem(20, 600, 64, dtype="bf16", seed=58, h_std=0.5, e_std=0.5, pos_per_row=(1, 3))
+    p["E"] = torch.full_like(p["E"], 0.125)  # every logit equal: the k smallest ids win
+    d = {key: v.cuda() for key, v in p.items()}
+    vals, ids, hits = topk(d["H"], d["E"], 8, d["row_offsets"], d["item_ids"], d["row_mask"])
+    assert (ids.cpu().numpy() == np.arange(8)).all()
+
+
+def test_hit_at_8_last_positions_sasrec876k():
+    """The evaluation shape: the last valid position of each sequence scored against all 876,000 items."""
+    cfg = W.CONFIGS["sasrec876k"]
+    p = W.make_problem(cfg, device="cuda")
+    m = p["row_mask"].cpu().numpy().reshape(cfg.B, cfg.N)
+    last = np.arange(cfg.B) * cfg.N + (cfg.N - 1)  # left padding: the last position of every sequence is valid
+    assert m.reshape(-1)[last].all()
+    H = p["H"][torch.from_numpy(last).cuda()].contiguous()
+    ro_all = p["row_offsets"].cpu().numpy()
+    ids_all = p["item_ids"].cpu().numpy()
+    pos = [ids_all[ro_all[r]:ro_all[r + 1]] for r in last]
+    ro = torch.from_numpy(np.concatenate([[0], np.cumsum([x.size for x in pos])]).astype(np.int32))
+    it = torch.from_numpy(np.concatenate(pos).astype(np.int32))
+    vals, ids, hits = topk(H, p["E"], 8, ro.cuda(), it.cuda())
+    torch.cuda.synchronize()
+    q = dict(H=H.cpu(), E=p["E"].cpu(), row_offsets=ro, item_ids=it, row_mask=torch.ones(cfg.B, dtype=torch.uint8))
+    _check(q, 8, vals.cpu().numpy(), ids.cpu().numpy(), hits.cpu().numpy(), rows=[0, 17, 77, 127])

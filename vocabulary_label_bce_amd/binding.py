@@ -31,7 +31,7 @@ class Problem(ctypes.Structure):
 
 
 EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
-           "cutbce_targets_to_csr",
+           "cutbce_targets_to_csr", "cutbce_topk",
            "cutbce_profile_enable", "cutbce_profile_read", "cutbce_status_string", "cutbce_version"]
 
 
@@ -51,6 +51,7 @@ def lib():
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
         L.cutbce_targets_to_csr.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp]
+        L.cutbce_topk.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
         L.cutbce_profile_enable.argtypes = [i32]
         L.cutbce_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), i32]
         L.cutbce_profile_enable.restype = i32
@@ -59,7 +60,7 @@ def lib():
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
         for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
-                  "cutbce_targets_to_csr"):
+                  "cutbce_targets_to_csr", "cutbce_topk"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -114,6 +115,13 @@ def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_sa
     _check(lib().cutbce_backward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
                                  _ptr(row_mask), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH), _ptr(dE), _ptr(ws),
                                  ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def topk(p: Problem, H, E, row_offsets, item_ids, row_mask, k: int, top_vals, top_ids, hits, ws, stream=None):
+    """cutbce_topk on device tensors: top_vals float [R, k], top_ids int32 [R, k], hits int32 [R] or None."""
+    _check(lib().cutbce_topk(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids), _ptr(row_mask),
+                             int(k), _ptr(top_vals), _ptr(top_ids), _ptr(hits), _ptr(ws),
+                             ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def targets_to_csr(targets, pad_id: int, row_offsets, item_ids, stream=None):

@@ -53,6 +53,7 @@ Layout make_layout(const cutbce_problem* p) {
   L.nb_i = L.n_vt * L.n_rs;
   // forward-sweep partials are indexed by unit: at most max(1024 units, every row tile once) x rows_per_wg
   const int64_t part_rows = (L.n_rt > 1024 ? L.n_rt : 1024) * (int64_t)L.rows_per_wg;
+  L.part_rows = part_rows;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -160,7 +161,7 @@ cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E
 
 extern "C" {
 
-int cutbce_version(void) { return 102; }
+int cutbce_version(void) { return 103; }
 
 const char* cutbce_status_string(cutbce_status s) {
   switch (s) {
@@ -247,6 +248,26 @@ cutbce_status cutbce_validate_targets(const cutbce_problem* p, const int32_t* ro
   if (!row_offsets || !bad || (p->nnz > 0 && !item_ids)) return CUTBCE_ERR_NULL;
   if (misaligned(row_offsets, 4) || misaligned(item_ids, 4) || misaligned(bad, 4)) return CUTBCE_ERR_ALIGN;
   return hip_status(launch_validate(p->rows, p->vocab, p->nnz, row_offsets, item_ids, bad, (hipStream_t)stream));
+}
+
+cutbce_status cutbce_topk(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
+                          const int32_t* item_ids, const uint8_t* row_mask, int32_t k, float* top_vals,
+                          int32_t* top_ids, int32_t* hits, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
+  if (s != CUTBCE_OK) return s;
+  if (!top_vals || !top_ids) return CUTBCE_ERR_NULL;
+  if (k < 1 || k > kTopKMax || k > p->vocab) return CUTBCE_ERR_SHAPE;
+  if (misaligned(top_vals, 4) || misaligned(top_ids, 4) || misaligned(hits, 4)) return CUTBCE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int kt = kTopKMax;
+  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_prep_h(L, ws, H, false, st));
+  TRY(launch_fill_i32((int32_t*)(ws + L.off_bptr_r), L.nb_r + 1, 0, st));  // no positive buckets
+  TRY(launch_topk_sweep(L, ws, E, kt, st));
+  TRY(launch_topk_finish(L, ws, row_mask, item_ids, kt, k, top_vals, top_ids, hits, st));
+  return CUTBCE_OK;
 }
 
 cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t* targets, int32_t pad_id,

@@ -86,6 +86,7 @@ struct Layout {
   size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan;
   size_t scan_elems;
+  int64_t part_rows;  // rows of the forward sweep's unit-major partial buffers
   size_t total;
 };
 
@@ -110,6 +111,12 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
                               float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, hipStream_t st);
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                               hipStream_t st);
+// full-vocabulary scoring: per-split top-kt lists (kt = kTopKMax entries kept) in the dH partial area
+constexpr int kTopKMax = 8;  // largest k of the scoring path (the paper evaluates Hit@8)
+hipError_t launch_topk_sweep(const Layout& L, char* ws, const void* E, int kt, hipStream_t st);
+hipError_t launch_topk_finish(const Layout& L, char* ws, const uint8_t* mask, const int32_t* item_ids, int kt, int k,
+                              float* vals, int32_t* ids, int32_t* hits, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_scale_dh(const Layout& L, const float* src, const float* grad_loss, void* dH, hipStream_t st);
 hipError_t launch_targets_to_csr(int64_t R, int L, const int32_t* targets, int32_t pad, int32_t* row_offsets,
                                  int32_t* item_ids, hipStream_t st);

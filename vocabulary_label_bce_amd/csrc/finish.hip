@@ -131,6 +131,108 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
   return hipGetLastError();
 }
 
+// Scoring finish (full-vocabulary top-k, the evaluation of "Cut Binary Cross Entropy" Section I-E): one wave
+// per row merges the S per-split top-KT lists of the forward sweep into the row's k best items -- larger
+// logit first, smaller item id among equal logits -- by k rounds of a wave-wide selection over candidates held
+// in registers, and counts how many of them are positives of the row (Hit@k: the row is a hit when the count is
+// non-zero). Masked rows get ids -1, logits -inf and count 0.
+constexpr int kMaxCandPerLane = kMaxSplits * kTopKMax / 64;  // S * KT / 64 with S <= 64, KT <= kTopKMax
+
+__device__ inline bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ void __launch_bounds__(256) k_topk_finish(const Ctl* __restrict__ ctl, const uint8_t* __restrict__ mask,
+                                                     const int32_t* __restrict__ compact_of,
+                                                     const int2* __restrict__ rptr,
+                                                     const int32_t* __restrict__ item_ids,
+                                                     const float* __restrict__ topv, const int32_t* __restrict__ topi,
+                                                     int64_t R, int RW, int KT, int k, float* __restrict__ vals,
+                                                     int32_t* __restrict__ ids, int32_t* __restrict__ hits) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = lane_id();
+  if (r >= R) return;
+  if (mask[r] == 0) {
+    if (lane < k) {
+      vals[r * k + lane] = -__builtin_inff();
+      ids[r * k + lane] = -1;
+    }
+    if (hits && lane == 0) hits[r] = 0;
+    return;
+  }
+  const int kc = compact_of[r];
+  const int S = ctl->splits;
+  const int Tt = (ctl->n_valid + RW - 1) / RW;
+  const int t = kc / RW, loc = kc % RW;
+  const int nc = S * KT;
+  float cv[kMaxCandPerLane];
+  int ci[kMaxCandPerLane];
+#pragma unroll
+  for (int m = 0; m < kMaxCandPerLane; ++m) {
+    const int c = lane + 64 * m;
+    cv[m] = -__builtin_inff();
+    ci[m] = -1;
+    if (c < nc) {
+      const int64_t at = ((int64_t)((c / KT) * Tt + t) * RW + loc) * KT + c % KT;
+      cv[m] = topv[at];
+      ci[m] = topi[at];
+    }
+  }
+  float last_v = __builtin_inff(), sel_v = -__builtin_inff();
+  int last_i = -1, sel_i = -1;
+  for (int q = 0; q < k; ++q) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < kMaxCandPerLane; ++m) {
+      const bool after = ci[m] >= 0 && ranks_before(last_v, last_i, cv[m], ci[m]);
+      if (after && ranks_before(cv[m], ci[m], bv, bi)) {
+        bv = cv[m];
+        bi = ci[m];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == q) {
+      sel_v = bv;
+      sel_i = bi;
+    }
+    last_v = bv;
+    last_i = bi;
+  }
+  if (lane < k) {
+    vals[r * k + lane] = sel_v;
+    ids[r * k + lane] = sel_i;
+  }
+  if (hits) {
+    bool hit = false;
+    if (lane < k) {
+      const int2 rp = rptr[kc];
+      for (int p = rp.x; p < rp.y; ++p) hit |= item_ids[p] == sel_i;
+    }
+    const uint64_t b = __ballot(hit);
+    if (lane == 0) hits[r] = __popcll(b);
+  }
+}
+
+hipError_t launch_topk_finish(const Layout& L, char* ws, const uint8_t* mask, const int32_t* item_ids, int kt, int k,
+                              float* vals, int32_t* ids, int32_t* hits, hipStream_t st) {
+  const unsigned blocks = (unsigned)((L.R + 3) / 4);
+  hipLaunchKernelGGL(k_topk_finish, dim3(blocks), dim3(256), 0, st, (const Ctl*)(ws + L.off_ctl), mask,
+                     (const int32_t*)(ws + L.off_compact_of), (const int2*)(ws + L.off_rptr), item_ids,
+                     (const float*)(ws + L.off_dhpart),
+                     (const int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * kt, L.R, L.rows_per_wg, kt, k,
+                     vals, ids, hits);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ void k_scale_dh(const float* __restrict__ src, const float* __restrict__ g, T* __restrict__ dst,
                            int64_t n) {

@@ -21,7 +21,7 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-static hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -378,7 +378,7 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   Ctl* ctl = (Ctl*)(ws + L.off_ctl);
   const int tile = rows_side ? L.rows_per_wg : L.items_per_wg;
   const int64_t minor = rows_side ? L.n_vs : L.n_rs;
-  hipError_t e = fill_i32(bptr, nb + 1, 0, st);
+  hipError_t e = launch_fill_i32(bptr, nb + 1, 0, st);
   if (e != hipSuccess) return e;
   const int64_t blocks = L.R_pad / 32;  // 32 rows of 8 lanes per 256-thread block
   if (L.nnz > 0) {
@@ -470,7 +470,7 @@ __global__ void k_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* __r
 
 hipError_t launch_validate(int64_t R, int64_t V, int64_t nnz, const int32_t* row_offsets,
                            const int32_t* item_ids, int32_t* bad, hipStream_t st) {
-  hipError_t e = fill_i32(bad, 1, 0, st);
+  hipError_t e = launch_fill_i32(bad, 1, 0, st);
   if (e != hipSuccess) return e;
   int64_t n = R > nnz ? R : nnz;
   int64_t blocks = (n + 255) / 256;

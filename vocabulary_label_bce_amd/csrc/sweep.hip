@@ -123,6 +123,39 @@ __device__ inline int choose_splits(int T, int n_steps, int P) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// Per-lane running top-KT list for full-vocabulary scoring: values in descending order, ids alongside. Items
+// reach a lane in increasing id order, so a strict comparison keeps the smaller id first among equal logits;
+// merging lists from other lanes or splits applies the full rule (larger logit, then smaller id).
+// ---------------------------------------------------------------------------------------------------------
+template <int KT>
+struct TopK {
+  float v[KT];
+  int id[KT];
+  __device__ inline void init() {
+#pragma unroll
+    for (int q = 0; q < KT; ++q) {
+      v[q] = -__builtin_inff();
+      id[q] = -1;
+    }
+  }
+  // insert (x, i) when it ranks before the last entry; `later` = every listed id is smaller than i
+  template <bool LATER>
+  __device__ inline void insert(float x, int i) {
+#pragma unroll
+    for (int q = 0; q < KT; ++q) {
+      const bool sw = LATER ? x > v[q] : (x > v[q] || (x == v[q] && (unsigned)i < (unsigned)id[q]));
+      const float tv = v[q];
+      const int ti = id[q];
+      v[q] = sw ? x : tv;
+      id[q] = sw ? i : ti;
+      x = sw ? tv : x;
+      i = sw ? ti : i;
+    }
+  }
+  __device__ inline float last() const { return v[KT - 1]; }
+};
+
+// ---------------------------------------------------------------------------------------------------------
 // Geometry of the step engine for (T, D, NW waves, GRAD = gradient GEMM present).
 //
 // The streamed operand moves through two LDS rings, one 32-row block per step: the d-packed block of step j
@@ -246,7 +279,7 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // iteration j - N into slot j % N and read at iteration j - 1; its slot-packed block is loaded at iteration
 // j - N + 2 into slot j % N and read at iteration j + 1. One barrier starts every iteration.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false>
+template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int KT = 0>
 struct Engine {
   using EL = Elem<T>;
   using G = Geo<T, D, NW, GRAD>;
@@ -318,7 +351,8 @@ struct Engine {
   // one G tile and the A operands of its next logit GEMM in registers. Barriers come only every kK
   // iterations, so the waves of a SIMD drift apart and one wave's vector work overlaps another's MFMAs. A last
   // iteration i = n finishes the pipeline (no loads, no logit GEMM).
-  __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz, int* met) {
+  __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz, int* met,
+                             TopK<KT ? KT : 1>* tk = nullptr) {
     const int n = j1 - j0;
     if (n <= 0) return;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // everyone is done with the previous unit's rings
@@ -342,13 +376,13 @@ struct Engine {
       top(0);
       z = logits(aop, own);
       read_a(1, aop);
-      epilogue(0, z, g, bq, e_acc, posz, met);
+      epilogue(0, z, g, bq, e_acc, posz, met, tk);
       for (int i = 1; i < n; ++i) {
         top(i);
         z = logits(aop, own);
         if (GRAD) grad(i - 1, g, acc);
         read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
-        epilogue(i, z, g, bq, e_acc, posz, met);
+        epilogue(i, z, g, bq, e_acc, posz, met, tk);
       }
     } else {
       // larger D: the logit GEMM of step i+1 runs in iteration i, reading its A operands from LDS right before
@@ -356,10 +390,10 @@ struct Engine {
       f32x16 za = logits_lds(0, own), zb;
       int i = 0;
       for (; i + 1 < n; i += 2) {
-        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met);
-        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz, met);
+        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met, tk);
+        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz, met, tk);
       }
-      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met);
+      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met, tk);
     }
     // iteration n: the slot-packed block of step n-1 must have landed
     wait_vm_and_barrier<0>();
@@ -369,11 +403,11 @@ struct Engine {
 
   // Iteration i of the larger-D schedule: Z(i+1) into zn, gradient GEMM of step i-1, epilogue of step i (zc).
   __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GPack<T>& g, f32x16* acc,
-                                  int* bq, float& e_acc, float& posz, int* met) {
+                                  int* bq, float& e_acc, float& posz, int* met, TopK<KT ? KT : 1>* tk) {
     top(i);
     if (i + 1 < n_steps()) zn = logits_lds(i + 1, own);
     if (GRAD && i > 0) grad(i - 1, g, acc);
-    epilogue(i, zc, g, bq, e_acc, posz, met);
+    epilogue(i, zc, g, bq, e_acc, posz, met, tk);
   }
   __device__ inline int n_steps() const { return j1 - j0; }
 
@@ -416,12 +450,29 @@ struct Engine {
   // loss sums (FWD), the G tile (GRAD) and, with MET, the Cut Metrics counts of the lane: met[0] logits
   // predicted positive (z > 0), met[1] positives predicted positive, met[2] positives.
   __device__ inline void epilogue(int j, const f32x16& z, GPack<T>& g, int* bq, float& e_acc, float& posz,
-                                  int* met) {
+                                  int* met, TopK<KT ? KT : 1>* tk) {
     bq[3] = bucket(j + 3);
     const int pb = __builtin_amdgcn_readfirstlane(bq[0]);
     const int pe = __builtin_amdgcn_readfirstlane(bq[1]);
 #pragma unroll
     for (int q = 0; q < 3; ++q) bq[q] = bq[q + 1];
+    if constexpr (KT > 0) {
+      // scoring: keep the lane's best items (real items only; the last step may hold padding). The lane's best
+      // new logit decides whether any insertion is needed; after the first steps it rarely is.
+      const int item0 = (j0 + j) * 32 + (lane / 32) * 4;
+      float x[16];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = item0 + (i / 4) * 8 + (i % 4) < nX ? z[i] : -__builtin_inff();  // item acc_pos(i, lane / 32)
+        mx = __builtin_fmaxf(mx, x[i]);
+      }
+      if (mx > tk->last()) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tk->template insert<true>(x[i], item0 + (i / 4) * 8 + (i % 4));
+      }
+      return;
+    }
     float c[16];
     if (FWD)
       epi_rows<GRAD, false>(z, 0u, c, e_acc, posz);
@@ -464,16 +515,18 @@ struct RowsArgs {
   float* dhpart;   // [units][RW][D]
   float2* rowpart; // [units][RW]
   int4* metpart;   // [units][RW]: Cut Metrics counts (predicted positive, true positive, positives)
+  float* topv;     // [units][RW][KT]: per-split top-KT logits (scoring)
+  int32_t* topi;   // [units][RW][KT]: their item ids
 };
 
 // ---------------------------------------------------------------------------------------------------------
 // Forward sweep. Persistent: gridDim.x workgroups (a multiple of 8, one per CU); units (split s, row tile t)
 // are assigned in contiguous per-XCD ranges so that the workgroups sharing an L2 stream the same part of E.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool WITH_DH, bool MET>
+template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   using EL = Elem<T>;
-  using EN = Engine<T, D, NW, true, WITH_DH, MET>;
+  using EN = Engine<T, D, NW, true, WITH_DH, MET, KT>;
   constexpr int RW = NW * 32, KS = D / EL::kK, NDB = D / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
@@ -518,11 +571,34 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     for (int db = 0; db < (WITH_DH ? NDB : 1); ++db) acc[db] = f32x16{};
     float e_acc = 0.f, posz = 0.f;
     int met[3] = {0, 0, 0};
+    TopK<KT ? KT : 1> tk;
+    if (KT) tk.init();
 
-    en.run(hop, acc, e_acc, posz, met);
+    en.run(hop, acc, e_acc, posz, met, &tk);
 
     // unit results: per-row loss parts and the dH partial of this split
     const int64_t urow = (int64_t)u * RW + wave * 32;  // row of the unit-major partial buffers
+    if constexpr (KT > 0) {
+      // merge the lists of the two lanes holding the row (the other lane's list is read whole before any
+      // insertion changes it), then one lane writes it
+      float ov[KT];
+      int oi[KT];
+#pragma unroll
+      for (int q = 0; q < KT; ++q) {
+        ov[q] = __shfl_xor(tk.v[q], 32, 64);
+        oi[q] = __shfl_xor(tk.id[q], 32, 64);
+      }
+#pragma unroll
+      for (int q = 0; q < KT; ++q) tk.template insert<false>(ov[q], oi[q]);
+      if (lane < 32) {
+#pragma unroll
+        for (int q = 0; q < KT; ++q) {
+          a.topv[(urow + lane) * KT + q] = tk.v[q];
+          a.topi[(urow + lane) * KT + q] = tk.id[q];
+        }
+      }
+      continue;
+    }
     const float e_tot = e_acc + __shfl_xor(e_acc, 32, 64);
     const float p_tot = posz + __shfl_xor(posz, 32, 64);
     if (lane < 32) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
@@ -633,7 +709,7 @@ static int cu_count() {
   return g_cus;
 }
 
-template <typename T, int D, int NW, bool WITH_DH, bool MET>
+template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT = 0>
 static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st) {
   using G = Geo<T, D, NW, WITH_DH>;
   RowsArgs a;
@@ -650,8 +726,12 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   a.dhpart = (float*)(ws + L.off_dhpart);
   a.rowpart = (float2*)(ws + L.off_rowpart);
   a.metpart = (int4*)(ws + L.off_metpart);
+  // scoring partials reuse the dH partial area: KT * 8 bytes per row <= D * 4 bytes
+  static_assert(KT * 8 <= D * 4, "top-k partials fit in the dH partial area");
+  a.topv = (float*)(ws + L.off_dhpart);
+  a.topi = (int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * (KT ? KT : 1);
   const size_t sm = G::kLdsBytes;
-  auto kern = k_rows<T, D, NW, WITH_DH, MET>;
+  auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   // persistent: as many workgroups as can be resident at once, a multiple of 8 (one range per XCD)
@@ -716,6 +796,16 @@ static hipError_t rows_any(const Layout& L, char* ws, const void* E, bool with_d
 
 hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
   CUTBCE_DISPATCH(L.dtype, rows_any, L, ws, E, with_dh, met, st);
+}
+
+template <typename T, int D, int NW>
+static hipError_t topk_any(const Layout& L, char* ws, const void* E, int kt, hipStream_t st) {
+  if (kt != kTopKMax) return hipErrorInvalidValue;
+  return rows_launch<T, D, NW, false, false, kTopKMax>(L, ws, E, st);
+}
+
+hipError_t launch_topk_sweep(const Layout& L, char* ws, const void* E, int kt, hipStream_t st) {
+  CUTBCE_DISPATCH(L.dtype, topk_any, L, ws, E, kt, st);
 }
 
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,

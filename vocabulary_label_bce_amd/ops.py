@@ -105,6 +105,31 @@ def cut_binary_cross_entropy(activations, embeddings, targets, weights=None, pad
     return cut_bce(H, embeddings, row_offsets, item_ids, mask)
 
 
+def topk(H, E, k: int = 8, row_offsets=None, item_ids=None, row_mask=None, ws=None):
+    """Full-vocabulary top-k of the logits H @ E^T per row, without materialising them (k <= 8): returns
+    (vals float32 [R, k], ids int32 [R, k], hits int32 [R] or None). With row_offsets / item_ids (CSR
+    positives) `hits` counts each row's positives among its k items (Hit@k = mean of hits > 0)."""
+    if not (H.is_cuda and E.is_cuda):
+        raise ValueError("topk runs on the GPU only")
+    R = H.shape[0]
+    dev = H.device
+    want_hits = row_offsets is not None
+    if row_offsets is None:
+        row_offsets = torch.zeros(R + 1, dtype=torch.int32, device=dev)
+        item_ids = torch.zeros(1, dtype=torch.int32, device=dev)
+    if row_mask is None:
+        row_mask = torch.ones(R, dtype=torch.uint8, device=dev)
+    H, E, row_offsets, item_ids, row_mask = _prep(H, E, row_offsets, item_ids, row_mask)
+    p = B.problem_of(H, E, item_ids)
+    if ws is None:
+        ws = B.alloc_workspace(p, dev)
+    vals = torch.empty(R, k, dtype=torch.float32, device=dev)
+    ids = torch.empty(R, k, dtype=torch.int32, device=dev)
+    hits = torch.empty(R, dtype=torch.int32, device=dev) if want_hits else None
+    B.topk(p, H, E, row_offsets, item_ids, row_mask, k, vals, ids, hits, ws)
+    return vals, ids, hits
+
+
 class Workspace:
     """Reusable explicit-call wrapper: one workspace per problem shape, outputs allocated once."""
 
