@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="instead of fwd+bwd, time full-vocabulary top-k scoring (cutbce_topk) of every valid row")
     ap.add_argument("--metrics", action="store_true",
                     help="also count the Cut Metrics (TP/FP/FN/TN per row) in the forward sweep")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -106,6 +108,55 @@ def load_traffic(kernel, workload):
     return d.get("bytes_per_launch")
 
 
+def bench_topk(a, cfg, prob, R_v):
+    """Full-vocabulary top-k scoring of every valid row of the workload (no [rows, V] buffer): 2*R_v*V*D flops."""
+    import torch
+
+    from vocabulary_label_bce_amd import binding as B
+    from vocabulary_label_bce_amd.ops import topk
+
+    H, E = prob["H"], prob["E"]
+    ro, ids, m = prob["row_offsets"], prob["item_ids"], prob["row_mask"]
+    V, D = E.shape
+    ws = B.alloc_workspace(B.problem_of(H, E, ids), H.device)
+    for _ in range(a.warmup):
+        out = topk(H, E, a.topk, ro, ids, m, ws=ws)
+    torch.cuda.synchronize()
+    B.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        out = topk(H, E, a.topk, ro, ids, m, ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = B.profile_read()
+    B.profile_enable(False)
+    ms = (t1 - t0) / a.steps * 1e3
+    F = 2.0 * R_v * V * D
+    tot, n = prof["topk_sweep"]
+    sweep_ms = tot / n if n else None
+    hits = out[2]
+    valid = m.bool()
+    print(json.dumps({
+        "metric": f"full-vocabulary top-{a.topk} scoring TFLOP/s (rows.V/s)",
+        "value": round(F / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": cfg.R, "valid_rows": R_v, "D": D, "V": V, "k": a.topk},
+        "rows_V_per_s": R_v * V / (ms * 1e-3),
+        "kernels": {"topk_sweep": {"avg_ms": round(sweep_ms, 4) if sweep_ms else None, "launches": n,
+                                   "tflops": round(F / (sweep_ms * 1e-3) / 1e12, 2) if sweep_ms else None}},
+        "hit_at_k_all_valid_rows": float((hits[valid] > 0).float().mean().item()),
+    }))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -129,6 +180,8 @@ def main():
     ro, ids, m = prob["row_offsets"], prob["item_ids"], prob["row_mask"]
     R_v = int(m.sum().item())
     V, D = E.shape
+    if a.topk:
+        return bench_topk(a, cfg, prob, R_v)
     w = Workspace(H, E, ids, want_row_loss=False, save_dh=True, want_metrics=a.metrics)
     g = torch.ones(1, dtype=torch.float32, device=dev)
 

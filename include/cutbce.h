@@ -137,10 +137,11 @@ cutbce_status cutbce_topk(const cutbce_problem *p, const void *H, const void *E,
 cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t *targets, int32_t pad_id,
                                     int32_t *row_offsets, int32_t *item_ids, void *stream);
 
-/* Opt-in kernel timing for benchmarks (host calls). While enabled, every launch of the two logit-tile sweeps
- * (kind 0: forward rows sweep, kind 1: backward dE sweep) is bracketed by HIP events recorded on the launch
- * stream. cutbce_profile_read waits for those events and returns, per kind, the summed milliseconds and the
- * number of launches since the last enable/read, then clears them. This is the only state the library keeps
+/* Opt-in kernel timing for benchmarks (host calls). While enabled, every launch of the logit-tile sweeps
+ * (kind 0: forward rows sweep, kind 1: backward dE sweep, kind 2: the scoring sweep of cutbce_topk) is
+ * bracketed by HIP events recorded on the launch stream. cutbce_profile_read waits for those events and
+ * returns, per kind, the summed milliseconds and the number of launches since the last enable/read, then
+ * clears them. This is the only state the library keeps
  * across calls; it is off by default. Enabling (on != 0) clears previous records; at most 65536 launches are
  * recorded (later ones are not timed). Not thread-safe. */
 cutbce_status cutbce_profile_enable(int on);

@@ -136,11 +136,11 @@ def validate_targets(p: Problem, row_offsets, item_ids, bad, stream=None):
                                          _stream(stream)))
 
 
-SWEEP_KINDS = ("rows_sweep", "items_sweep")
+SWEEP_KINDS = ("rows_sweep", "items_sweep", "topk_sweep")
 
 
 def profile_enable(on: bool = True):
-    """Start (or stop) event timing of the two sweep kernels inside the library."""
+    """Start (or stop) event timing of the sweep kernels inside the library."""
     _check(lib().cutbce_profile_enable(1 if on else 0))
 
 

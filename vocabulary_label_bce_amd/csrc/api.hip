@@ -265,7 +265,12 @@ cutbce_status cutbce_topk(const cutbce_problem* p, const void* H, const void* E,
   TRY(launch_compact(L, ws, row_mask, row_offsets, st));
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_fill_i32((int32_t*)(ws + L.off_bptr_r), L.nb_r + 1, 0, st));  // no positive buckets
-  TRY(launch_topk_sweep(L, ws, E, kt, st));
+  {
+    ProfRec* r = prof_begin(2, st);
+    const hipError_t e = launch_topk_sweep(L, ws, E, kt, st);
+    prof_end(r, st);
+    TRY(e);
+  }
   TRY(launch_topk_finish(L, ws, row_mask, item_ids, kt, k, top_vals, top_ids, hits, st));
   return CUTBCE_OK;
 }

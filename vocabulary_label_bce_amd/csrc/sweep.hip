@@ -459,17 +459,21 @@ struct Engine {
     if constexpr (KT > 0) {
       // scoring: keep the lane's best items (real items only; the last step may hold padding). The lane's best
       // new logit decides whether any insertion is needed; after the first steps it rarely is.
+      // Only the values above the lane's current k-th best are inserted, one at a time, picked by a select
+      // chain (no dynamic register indexing).
       const int item0 = (j0 + j) * 32 + (lane / 32) * 4;
-      float x[16];
-      float mx = -__builtin_inff();
+      const float thr = tk->last();
+      uint32_t cand = 0u;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = item0 + (i / 4) * 8 + (i % 4) < nX ? z[i] : -__builtin_inff();  // item acc_pos(i, lane / 32)
-        mx = __builtin_fmaxf(mx, x[i]);
-      }
-      if (mx > tk->last()) {
+      for (int i = 0; i < 16; ++i)
+        cand |= (z[i] > thr && item0 + (i / 4) * 8 + (i % 4) < nX) ? (1u << i) : 0u;  // item acc_pos(i, lane / 32)
+      while (cand) {
+        const int i = __builtin_ctz(cand);
+        cand &= cand - 1u;
+        float x = z[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tk->template insert<true>(x[i], item0 + (i / 4) * 8 + (i % 4));
+        for (int q = 1; q < 16; ++q) x = i == q ? z[q] : x;
+        tk->template insert<true>(x, item0 + (i / 4) * 8 + (i % 4));
       }
       return;
     }
