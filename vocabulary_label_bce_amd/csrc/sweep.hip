@@ -14,11 +14,14 @@
 // which is what carries the gradient signal when logits are small.
 //
 // Both sweeps share one software-pipelined step engine. Iteration i of a wave issues the MFMAs of the logit
-// tile of step i+1 and of the gradient GEMM of step i-1, while the VALU evaluates the epilogue of step i; the
-// three are independent, so the matrix cores and the vector ALU work at the same time. Streamed operands
-// reach LDS by direct buffer loads (global -> LDS, no registers) into two rings, one for the d-packed operand
-// of the logit GEMM and one for the slot-packed operand of the gradient GEMM, with one workgroup barrier per
-// step.
+// tile of step i and of the gradient GEMM of step i-1, then reads the operands of step i+1 and evaluates the
+// epilogue of step i on the vector ALU; none depends on another, so while one wave runs its MFMAs the other
+// wave of the SIMD can run its vector work. Streamed operands reach LDS by direct buffer loads (global -> LDS,
+// no registers) into two rings, one for the d-packed operand of the logit GEMM and one for the slot-packed
+// operand of the gradient GEMM; workgroup barriers come every few steps (see Geo).
+//
+// The forward sweep also serves full-vocabulary scoring (top-k per row, Section I-E's evaluation) with a
+// running top list per lane in place of the loss epilogue, and can count the Cut Metrics of Section III-D.
 #include "common.h"
 
 namespace cutbce {
@@ -51,10 +54,6 @@ template <> struct GPack<__bf16> {
 #pragma unroll
       for (int j = 0; j < 8; ++j) g[q][j] = (__bf16)c[q * 8 + j];
   }
-  __device__ inline void zero() {
-    g[0] = bf16x8{};
-    g[1] = bf16x8{};
-  }
   __device__ inline bf16x8 op(int q) const { return g[q]; }
 };
 template <> struct GPack<float> {
@@ -62,10 +61,6 @@ template <> struct GPack<float> {
   __device__ inline void set(const float* c) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) g[i] = c[i];
-  }
-  __device__ inline void zero() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = 0.f;
   }
   __device__ inline float op(int q) const { return g[q]; }
 };
@@ -524,8 +519,9 @@ struct RowsArgs {
 };
 
 // ---------------------------------------------------------------------------------------------------------
-// Forward sweep. Persistent: gridDim.x workgroups (a multiple of 8, one per CU); units (split s, row tile t)
-// are assigned in contiguous per-XCD ranges so that the workgroups sharing an L2 stream the same part of E.
+// Forward sweep. Persistent: gridDim.x workgroups (as many as can be resident, a multiple of 8); units (split s,
+// row tile t) are assigned in contiguous per-XCD ranges so that the workgroups sharing an L2 stream the same
+// part of E. With KT > 0 it scores instead: per-lane top-KT lists, merged per row and written per unit.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
