@@ -28,8 +28,9 @@
  *     synchronises with the host. Scalars that the device produces or consumes (loss, grad_loss) stay in
  *     device memory.
  *   - Host-side argument checks run before anything is enqueued; on any error nothing is enqueued and the
- *     outputs are untouched. Ids outside [0, V) or inconsistent row_offsets are not checked by the compute
- *     entry points (they are skipped if encountered); cutbce_validate_targets checks them on the device.
+ *     outputs are untouched. Ids outside [0, V) are skipped by the compute entry points, and row offsets are
+ *     clamped into [0, nnz] (a decreasing range is empty), so malformed targets never cause reads outside
+ *     item_ids; cutbce_validate_targets reports them on the device.
  *   - Results are deterministic: the same inputs on the same device give bitwise identical outputs (no
  *     floating-point atomics).
  *   - The workspace is scratch: its contents on entry are ignored and on return are unspecified. Concurrent

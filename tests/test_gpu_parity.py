@@ -235,3 +235,25 @@ def test_config_catalog10m_sampled():
     # the workspace never holds a [rows, V] buffer: it is far below the dense logits size
     cfg = W.CONFIGS["catalog10m"]
     assert w.ws.numel() < 0.05 * W.dense_logits_bytes(cfg.R, cfg.V)
+
+
+def test_malformed_offsets_are_clamped():
+    """Row offsets past nnz or decreasing: the library reads only inside item_ids (ranges clamped into
+    [0, nnz], a decreasing range is empty) and matches the oracle on the clamped targets."""
+    p = W.custom_problem(40, 500, 64, dtype="bf16", seed=61, h_std=0.4, e_std=0.4, pos_per_row=(1, 5))
+    ro = p["row_offsets"].numpy().astype(np.int64)
+    nnz = int(ro[-1])
+    bad = ro.copy()
+    bad[10] = bad[12] + 3  # row 9 ends past row 10's start, row 10 has a decreasing range
+    bad[-1] = nnz + 50     # the last row runs past nnz
+    lo = np.clip(bad[:-1], 0, nnz)
+    hi = np.maximum(np.clip(bad[1:], 0, nnz), lo)
+    ids = p["item_ids"].numpy()
+    rows = [ids[a:b] for a, b in zip(lo, hi)]
+    q = dict(p)
+    q["row_offsets"] = torch.from_numpy(np.concatenate([[0], np.cumsum([x.size for x in rows])]).astype(np.int32))
+    q["item_ids"] = torch.from_numpy(np.concatenate(rows).astype(np.int32))
+    ref = oracle.full(q["H"], q["E"], q["row_offsets"], q["item_ids"], q["row_mask"], g=1.0)
+    pb = dict(p)
+    pb["row_offsets"] = torch.from_numpy(bad.astype(np.int32))
+    _check(p, _run(pb, g=1.0), ref)

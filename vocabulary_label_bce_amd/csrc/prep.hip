@@ -57,8 +57,8 @@ __device__ inline int block_excl_scan(int v, int* sh, int& total) {
 // ---------------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask,
                                                   const int32_t* __restrict__ row_offsets, int64_t R,
-                                                  int64_t R_pad, int64_t V, Ctl* ctl, int32_t* row_of,
-                                                  int32_t* compact_of, int2* rptr) {
+                                                  int64_t R_pad, int64_t V, int64_t nnz, Ctl* ctl,
+                                                  int32_t* row_of, int32_t* compact_of, int2* rptr) {
   __shared__ int sh[16];
   const int tid = threadIdx.x;
   int base = 0;
@@ -80,7 +80,10 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
         if (f[j]) {
           row_of[k] = (int32_t)r;
           compact_of[r] = k;
-          rptr[k] = make_int2(row_offsets[r], row_offsets[r + 1]);
+          // the row's id range, clamped into [0, nnz] (inconsistent offsets give an empty or shortened range)
+          const int64_t b = row_offsets[r] < 0 ? 0 : (row_offsets[r] > nnz ? nnz : row_offsets[r]);
+          const int64_t e = row_offsets[r + 1] < b ? b : (row_offsets[r + 1] > nnz ? nnz : row_offsets[r + 1]);
+          rptr[k] = make_int2((int)b, (int)e);
           ++k;
         } else {
           compact_of[r] = -1;
@@ -104,7 +107,7 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
 
 hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const int32_t* row_offsets,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, row_offsets, L.R, L.R_pad, L.V,
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, row_offsets, L.R, L.R_pad, L.V, L.nnz,
                      (Ctl*)(ws + L.off_ctl), (int32_t*)(ws + L.off_row_of), (int32_t*)(ws + L.off_compact_of),
                      (int2*)(ws + L.off_rptr));
   return hipGetLastError();
