@@ -293,6 +293,14 @@ struct Engine {
   int own0;  // first owner index of this wave (compact row or item)
   int j0, j1;
 
+  uint32_t lds_s;  // LDS byte address of `lds`, wave-uniform (scalar): DMA destinations are formed in SGPRs
+
+  __device__ inline void setup(char* l, int w, int ln) {
+    lds = l;
+    wave = __builtin_amdgcn_readfirstlane(w);
+    lane = ln;
+    lds_s = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void*)l);
+  }
   __device__ inline char* ringA(int rel) const { return lds + (rel % G::kNA) * G::kStepBytes; }
   __device__ inline char* ringB(int rel) const {
     return lds + (G::kNA + rel % (G::kNB ? G::kNB : 1)) * G::kStepBytes;
@@ -302,14 +310,15 @@ struct Engine {
   }
   __device__ inline int clampj(int rel) const { return j0 + rel < j1 ? j0 + rel : j1 - 1; }
 
-  // d-packed block of step j0 + rel into A slot rel % NA (rows >= nX read as zero).
-  __device__ inline void dma_a(int rel) const {
+  // d-packed block of step j0 + rel into A slot `slot` = rel % NA (rows >= nX read as zero).
+  __device__ inline void dma_a(int rel) const { dma_a(rel, rel % G::kNA); }
+  __device__ inline void dma_a(int rel, int slot) const {
     const int64_t row0 = (int64_t)clampj(rel) * 32;
     const char* xa = (const char*)X + row0 * (int64_t)(D * G::kEsz);
     const int64_t rem = (nX - row0) * (int64_t)(D * G::kEsz);
     const int nrec = rem <= 0 ? 0 : (rem > (int64_t)G::kStepBytes ? G::kStepBytes : (int)rem);
     __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)xa, (short)0, nrec, 0x00020000);
-    char* dst = ringA(rel);
+    const uint32_t dst = lds_s + slot * G::kStepBytes;
 #pragma unroll
     for (int q = 0; q < G::kLoadsPerPart; ++q) {
       const int inst = wave + q * NW;                           // wave instruction index within the block
@@ -318,20 +327,21 @@ struct Engine {
       const int within = pos % (D * G::kEsz);
       const int lchunk = (within / 16) ^ swz<G::kCPR>(row);
       const int voff = row * (D * G::kEsz) + lchunk * 16 + within % 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + inst * G::kWaveBytes), G::kLoadB, voff, 0, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(size_t)(dst + inst * G::kWaveBytes), G::kLoadB, voff,
+                                               0, 0, 0);
     }
   }
-  // slot-packed block of step j0 + rel into B slot rel % NB (a contiguous copy).
-  __device__ inline void dma_b(int rel) const {
+  // slot-packed block of step j0 + rel into B slot `slot` = rel % NB (a contiguous copy).
+  __device__ inline void dma_b(int rel) const { dma_b(rel, rel % (G::kNB ? G::kNB : 1)); }
+  __device__ inline void dma_b(int rel, int slot) const {
     const int64_t row0 = (int64_t)clampj(rel) * 32;
     const char* xb = (const char*)Xsp + row0 * (int64_t)(D * G::kEsz);
     __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, G::kStepBytes, 0x00020000);
-    char* dst = ringB(rel);
+    const uint32_t dst = lds_s + (G::kNA + slot) * G::kStepBytes;
 #pragma unroll
     for (int q = 0; q < G::kLoadsPerPart; ++q) {
       const int inst = wave + q * NW;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + inst * G::kWaveBytes), G::kLoadB,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(size_t)(dst + inst * G::kWaveBytes), G::kLoadB,
                                                inst * G::kWaveBytes + lane * G::kLoadB, 0, 0, 0);
     }
   }
@@ -372,12 +382,23 @@ struct Engine {
       z = logits(aop, own);
       read_a(1, aop);
       epilogue(0, z, g, bq, e_acc, posz, met, tk);
+      // ring slots of iteration i, advanced without divisions: the A block loaded now, the B block loaded now,
+      // the A block read now (step i+1) and the B block read now (step i-1)
+      int sdA = (1 + G::kLA) % G::kNA, sdB = GRAD ? (1 + G::kLB) % G::kNB : 0, srA = 2 % G::kNA, srB = 0;
       for (int i = 1; i < n; ++i) {
-        top(i);
+        if (G::kK == 1 || i % G::kK == 0) wait_vm_and_barrier<G::kInFlight>();
+        dma_a(i + G::kLA, sdA);
+        if (GRAD) dma_b(i + G::kLB, sdB);
         z = logits(aop, own);
-        if (GRAD) grad(i - 1, g, acc);
-        read_a(i + 1, aop);  // step n's slot holds a clamped copy of step n-1: harmless
+        if (GRAD) grad_slot(srB, g, acc);
+        read_slot(srA, aop);  // step n's slot holds a clamped copy of step n-1: harmless
         epilogue(i, z, g, bq, e_acc, posz, met, tk);
+        sdA = sdA + 1 == G::kNA ? 0 : sdA + 1;
+        srA = srA + 1 == G::kNA ? 0 : srA + 1;
+        if (GRAD) {
+          sdB = sdB + 1 == G::kNB ? 0 : sdB + 1;
+          srB = srB + 1 == G::kNB ? 0 : srB + 1;
+        }
       }
     } else {
       // larger D: the logit GEMM of step i+1 runs in iteration i, reading its A operands from LDS right before
@@ -413,8 +434,9 @@ struct Engine {
     if (GRAD) dma_b(i + G::kLB);
   }
 
-  __device__ inline void read_a(int i, Op* aop) const {
-    const char* a = ringA(i);
+  __device__ inline void read_a(int i, Op* aop) const { read_slot(i % G::kNA, aop); }
+  __device__ inline void read_slot(int slot, Op* aop) const {
+    const char* a = lds + slot * G::kStepBytes;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) aop[ks] = lds_a<T, D>(a, lane % 32, ks, lane);
   }
@@ -434,7 +456,10 @@ struct Engine {
   }
 
   __device__ inline void grad(int j, const GPack<T>& g, f32x16* acc) const {
-    const char* b = ringB(j);
+    grad_slot(j % (G::kNB ? G::kNB : 1), g, acc);
+  }
+  __device__ inline void grad_slot(int slot, const GPack<T>& g, f32x16* acc) const {
+    const char* b = lds + (G::kNA + slot) * G::kStepBytes;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -544,9 +569,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   const int start = (int)(((int64_t)x * U) / 8), cnt = (int)(((int64_t)(x + 1) * U) / 8) - start;
 
   EN en;
-  en.lds = lds;
-  en.wave = wave;
-  en.lane = lane;
+  en.setup(lds, wave, lane);
   en.X = (const T*)a.E;
   en.Xsp = (const T*)a.Evp;
   en.nX = a.V;
@@ -662,9 +685,7 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   const int n_st = (n_valid + 31) / 32;
   if (n_st > 0) {
     EN en;
-    en.lds = lds;
-    en.wave = wave;
-    en.lane = lane;
+    en.setup(lds, wave, lane);
     en.X = (const T*)a.Hc;
     en.Xsp = (const T*)a.Hrp;
     en.nX = n_valid;
