@@ -180,7 +180,9 @@ struct Geo {
   static constexpr int kLoadB = (kStepBytes / NW >= 1024) ? 16 : 4;  // bytes per lane per DMA load
   static constexpr int kWaveBytes = 64 * kLoadB;                     // bytes one wave instruction moves
   static constexpr int kLoadsPerPart = kStepBytes / kWaveBytes / NW;
-  static constexpr int kLoadsPerIter = kLoadsPerPart * (GRAD ? 2 : 1) + 1;  // + the bucket-pointer load
+  // vector-memory loads an iteration issues (ring blocks; the bucket-pointer loads come once per 64 steps and
+  // only make the following barrier wait longer)
+  static constexpr int kLoadsPerIter = kLoadsPerPart * (GRAD ? 2 : 1);
   static constexpr int kInFlight = kS ? kLoadsPerIter : 0;  // loads a barrier lets stay in flight
   static constexpr int kLdsBytes = (kNA + kNB) * kStepBytes + NW * 256;
   static_assert(kLoadsPerPart >= 1 && kStepBytes % (kWaveBytes * NW) == 0, "load split");
@@ -219,24 +221,42 @@ __device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int
 // With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives) = sign(z) (1/(1+e^-|z|) - 1/2).
 template <bool GRAD, bool HASPOS>
 __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e_acc, float& posz) {
-  // u_i = -|z_i| log2(e); 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow. Pairwise
-  // products and sums keep the dependency chains short.
+  // u_i = -|z_i| log2(e); w_i = 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow. The
+  // product is formed over adjacent pairs, then quads, then the whole tile (the sum of u alongside).
   float u[16], w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     u[i] = __builtin_fabsf(z[i]) * -kLog2e;
     w[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
-    if (GRAD) c[i] = __builtin_copysignf(__builtin_amdgcn_rcpf(w[i]) - 0.5f, z[i]);
+  }
+  float w2[8], w4[4], u2[8], u4[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w2[i] = w[2 * i] * w[2 * i + 1];
+    u2[i] = u[2 * i] + u[2 * i + 1];
   }
 #pragma unroll
-  for (int h = 8; h >= 1; h /= 2)
+  for (int i = 0; i < 4; ++i) {
+    w4[i] = w2[2 * i] * w2[2 * i + 1];
+    u4[i] = u2[2 * i] + u2[2 * i + 1];
+  }
+  if (GRAD) {
+    // 1/w_i from one reciprocal per quad (batch inversion down the product tree):
+    // 1/(w0 w1) = w2 w3 / (w0 w1 w2 w3), 1/w0 = w1 / (w0 w1), ...; each 1/w_i picks up two extra roundings.
+    // c_i = sigma(z_i) - 1/2 = sign(z_i) (1/w_i - 1/2).
 #pragma unroll
-    for (int i = 0; i < h; ++i) {
-      w[i] *= w[i + h];
-      u[i] += u[i + h];
+    for (int q = 0; q < 4; ++q) {
+      const float r4 = __builtin_amdgcn_rcpf(w4[q]);
+      const float ra = r4 * w2[2 * q + 1], rb = r4 * w2[2 * q];
+      const float r[4] = {ra * w[4 * q + 1], ra * w[4 * q], rb * w[4 * q + 3], rb * w[4 * q + 2]};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(r[k] - 0.5f, z[4 * q + k]);
     }
+  }
+  const float wp = (w4[0] * w4[1]) * (w4[2] * w4[3]);
+  const float up = (u4[0] + u4[1]) + (u4[2] + u4[3]);
   // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2] = ln 2 * (log2(prod) - 16 - sum_i u_i / 2)
-  e_acc += kLn2 * (__builtin_amdgcn_logf(w[0]) - 16.f - 0.5f * u[0]);
+  e_acc += kLn2 * (__builtin_amdgcn_logf(wp) - 16.f - 0.5f * up);
   if (HASPOS) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -302,9 +322,6 @@ struct Engine {
     lds_s = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void*)l);
   }
   __device__ inline char* ringA(int rel) const { return lds + (rel % G::kNA) * G::kStepBytes; }
-  __device__ inline char* ringB(int rel) const {
-    return lds + (G::kNA + rel % (G::kNB ? G::kNB : 1)) * G::kStepBytes;
-  }
   __device__ inline uint32_t* lmask() const {
     return (uint32_t*)(lds + (G::kNA + G::kNB) * G::kStepBytes) + wave * 64;
   }
@@ -345,7 +362,38 @@ struct Engine {
                                                inst * G::kWaveBytes + lane * G::kLoadB, 0, 0, 0);
     }
   }
-  __device__ inline int bucket(int rel) const { return bptr[bbase + (j0 + rel < j1 ? j0 + rel : j1)]; }
+  // Bucket pointers, 64 steps at a time: lane l of block b holds those of step 64b + l (bk_lo) and of the step
+  // after it (bk_hi); a step reads its pair with two lane reads. The next block is loaded a whole block ahead,
+  // so no step waits on a recent load (a load consumed one step after it is issued would make the wave wait
+  // for every earlier memory operation, the ring loads included).
+  int bk_lo, bk_hi, bn_lo, bn_hi;
+  __device__ inline void bkt_load(int b, int& lo, int& hi) const {
+    int x = j0 + 64 * b + lane;
+    x = x < j1 - 1 ? x : j1 - 1;  // steps past the unit are never used
+    lo = bptr[bbase + x];
+    hi = bptr[bbase + x + 1];
+  }
+  __device__ inline void bkt_init() {
+    bkt_load(0, bk_lo, bk_hi);
+    bkt_load(1, bn_lo, bn_hi);
+  }
+  // Step j > 0 starts block j / 64 (j % 64 == 0). Steps that are multiples of 64 are barrier iterations (kK
+  // divides 64), so this rare refill sits in the barrier's branch and adds none to the other iterations.
+  __device__ inline void bkt_next(int j) {
+    bk_lo = bn_lo;
+    bk_hi = bn_hi;
+    bkt_load((j >> 6) + 1, bn_lo, bn_hi);
+  }
+  __device__ inline void bkt_get(int j, int& pb, int& pe) const {
+    pb = __builtin_amdgcn_readlane(bk_lo, j & 63);
+    pe = __builtin_amdgcn_readlane(bk_hi, j & 63);
+  }
+  // Start of iteration j's barrier (taken when j % kK == 0), with the bucket block refill it carries.
+  __device__ inline void barrier_at(int j) {
+    static_assert(64 % G::kK == 0, "bucket blocks start on barrier iterations");
+    wait_vm_and_barrier<G::kInFlight>();
+    if ((j & 63) == 0 && j > 0) bkt_next(j);
+  }
 
   // Runs the sweep; `own` holds the owner operand for every k-step. On return acc holds the gradient tile
   // (GRAD) and e_acc / posz the forward row sums (FWD).
@@ -367,9 +415,7 @@ struct Engine {
 #pragma unroll
       for (int q = 0; q < G::kLB; ++q) dma_b(q);
     }
-    int bq[4];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q] = bucket(q);
+    bkt_init();
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
     GPack<T> g;  // G tile whose gradient GEMM is pending
@@ -379,20 +425,23 @@ struct Engine {
       f32x16 z;  // logit tile whose epilogue is pending
       read_a(0, aop);
       top(0);
+      int pb, pe;
+      bkt_get(0, pb, pe);
       z = logits(aop, own);
       read_a(1, aop);
-      epilogue(0, z, g, bq, e_acc, posz, met, tk);
+      epilogue(0, pb, pe, z, g, e_acc, posz, met, tk);
       // ring slots of iteration i, advanced without divisions: the A block loaded now, the B block loaded now,
       // the A block read now (step i+1) and the B block read now (step i-1)
       int sdA = (1 + G::kLA) % G::kNA, sdB = GRAD ? (1 + G::kLB) % G::kNB : 0, srA = 2 % G::kNA, srB = 0;
       for (int i = 1; i < n; ++i) {
-        if (G::kK == 1 || i % G::kK == 0) wait_vm_and_barrier<G::kInFlight>();
+        if (G::kK == 1 || i % G::kK == 0) barrier_at(i);
         dma_a(i + G::kLA, sdA);
         if (GRAD) dma_b(i + G::kLB, sdB);
+        bkt_get(i, pb, pe);
         z = logits(aop, own);
         if (GRAD) grad_slot(srB, g, acc);
         read_slot(srA, aop);  // step n's slot holds a clamped copy of step n-1: harmless
-        epilogue(i, z, g, bq, e_acc, posz, met, tk);
+        epilogue(i, pb, pe, z, g, e_acc, posz, met, tk);
         sdA = sdA + 1 == G::kNA ? 0 : sdA + 1;
         srA = srA + 1 == G::kNA ? 0 : srA + 1;
         if (GRAD) {
@@ -406,10 +455,10 @@ struct Engine {
       f32x16 za = logits_lds(0, own), zb;
       int i = 0;
       for (; i + 1 < n; i += 2) {
-        step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met, tk);
-        step_lds(i + 1, own, zb, za, g, acc, bq, e_acc, posz, met, tk);
+        step_lds(i, own, za, zb, g, acc, e_acc, posz, met, tk);
+        step_lds(i + 1, own, zb, za, g, acc, e_acc, posz, met, tk);
       }
-      if (i < n) step_lds(i, own, za, zb, g, acc, bq, e_acc, posz, met, tk);
+      if (i < n) step_lds(i, own, za, zb, g, acc, e_acc, posz, met, tk);
     }
     // iteration n: the slot-packed block of step n-1 must have landed
     wait_vm_and_barrier<0>();
@@ -419,17 +468,19 @@ struct Engine {
 
   // Iteration i of the larger-D schedule: Z(i+1) into zn, gradient GEMM of step i-1, epilogue of step i (zc).
   __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GPack<T>& g, f32x16* acc,
-                                  int* bq, float& e_acc, float& posz, int* met, TopK<KT ? KT : 1>* tk) {
+                                  float& e_acc, float& posz, int* met, TopK<KT ? KT : 1>* tk) {
     top(i);
+    int pb, pe;
+    bkt_get(i, pb, pe);
     if (i + 1 < n_steps()) zn = logits_lds(i + 1, own);
     if (GRAD && i > 0) grad(i - 1, g, acc);
-    epilogue(i, zc, g, bq, e_acc, posz, met, tk);
+    epilogue(i, pb, pe, zc, g, e_acc, posz, met, tk);
   }
   __device__ inline int n_steps() const { return j1 - j0; }
 
   // Start of iteration i: the barrier (every kK iterations) and the loads of the iteration.
   __device__ inline void top(int i) {
-    if (G::kK == 1 || i % G::kK == 0) wait_vm_and_barrier<G::kInFlight>();
+    if (G::kK == 1 || i % G::kK == 0) barrier_at(i);
     dma_a(i + G::kLA);
     if (GRAD) dma_b(i + G::kLB);
   }
@@ -466,16 +517,11 @@ struct Engine {
       for (int q = 0; q < EL::kGroups; ++q) acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, db, q, lane), acc[db]);
   }
 
-  // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step from the bucket FIFO,
+  // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step (bucket [pb, pe)),
   // loss sums (FWD), the G tile (GRAD) and, with MET, the Cut Metrics counts of the lane: met[0] logits
   // predicted positive (z > 0), met[1] positives predicted positive, met[2] positives.
-  __device__ inline void epilogue(int j, const f32x16& z, GPack<T>& g, int* bq, float& e_acc, float& posz,
+  __device__ inline void epilogue(int j, int pb, int pe, const f32x16& z, GPack<T>& g, float& e_acc, float& posz,
                                   int* met, TopK<KT ? KT : 1>* tk) {
-    bq[3] = bucket(j + 3);
-    const int pb = __builtin_amdgcn_readfirstlane(bq[0]);
-    const int pe = __builtin_amdgcn_readfirstlane(bq[1]);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q] = bq[q + 1];
     if constexpr (KT > 0) {
       // scoring: keep the lane's best items (real items only; the last step may hold padding). The lane's best
       // new logit decides whether any insertion is needed; after the first steps it rarely is.
