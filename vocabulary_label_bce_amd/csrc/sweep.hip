@@ -164,6 +164,9 @@ struct TopK {
 //   kNA >= kLA + kK - 1, kNB >= kLB + kK + 1     (a barrier separates the last read of a slot from its
 //                                                 refill).
 // ---------------------------------------------------------------------------------------------------------
+#ifndef CUTBCE_LOAD_SLACK
+#define CUTBCE_LOAD_SLACK 1  // iterations whose ring loads a barrier lets stay in flight (steps up to 16 KB)
+#endif
 #ifndef CUTBCE_STEPS_PER_BARRIER
 #define CUTBCE_STEPS_PER_BARRIER 0  // 0: by step size
 #endif
@@ -173,7 +176,7 @@ struct Geo {
   static constexpr int kStepBytes = 32 * D * kEsz;  // one 32-row block of an operand
   static constexpr int kK = CUTBCE_STEPS_PER_BARRIER > 0 ? (kStepBytes <= 8192 ? CUTBCE_STEPS_PER_BARRIER : 1)
                             : (kStepBytes <= 4096 ? 4 : kStepBytes <= 8192 ? 2 : 1);
-  static constexpr int kS = kStepBytes <= 16384 ? 1 : 0;
+  static constexpr int kS = kStepBytes <= 16384 ? CUTBCE_LOAD_SLACK : 0;
   static constexpr int kLA = kK + 1 + kS, kLB = kK - 1 + kS;
   static constexpr int kNA = kLA + kK - 1, kNB = GRAD ? kLB + kK + 1 : 0;
   static constexpr int kCPR = D * kEsz / 16;                         // 16-byte chunks per d-packed row
@@ -183,7 +186,7 @@ struct Geo {
   // vector-memory loads an iteration issues (ring blocks; the bucket-pointer loads come once per 64 steps and
   // only make the following barrier wait longer)
   static constexpr int kLoadsPerIter = kLoadsPerPart * (GRAD ? 2 : 1);
-  static constexpr int kInFlight = kS ? kLoadsPerIter : 0;  // loads a barrier lets stay in flight
+  static constexpr int kInFlight = kS * kLoadsPerIter;  // loads a barrier lets stay in flight
   static constexpr int kLdsBytes = (kNA + kNB) * kStepBytes + NW * 256;
   static_assert(kLoadsPerPart >= 1 && kStepBytes % (kWaveBytes * NW) == 0, "load split");
   static_assert(kLoadsPerIter <= 63, "vmcnt range");
@@ -697,6 +700,8 @@ struct ItemsArgs {
   const float* grad_loss;
   void* dE;
   int64_t V, n_rs;
+  int n_full;        // item tiles swept whole; the tiles after them are swept in two row halves
+  float* tailpart;   // [split tile][half][IW][D] fp32 partial sums of the halved tiles
 };
 
 // ---------------------------------------------------------------------------------------------------------
@@ -711,7 +716,13 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   const T* __restrict__ E = (const T*)a.E;
 
-  const int t = blockIdx.x;
+  // Workgroups below n_full sweep a whole tile. The last tiles (fewer than half a round of workgroups) are
+  // swept in two row halves by two workgroups each, which shortens the final round; their partial sums are
+  // added by k_items_tail.
+  const int b = blockIdx.x;
+  const int split = b >= a.n_full ? (b - a.n_full) / 2 : -1;  // index among the halved tiles
+  const int part = b >= a.n_full ? (b - a.n_full) % 2 : 0;
+  const int t = split < 0 ? b : a.n_full + split;
   const int64_t v_own0 = (int64_t)t * IW + wave * 32;  // first item of this wave
   const int64_t v_mine = v_own0 + lane % 32;
   typename EL::Op eop[KS];
@@ -739,10 +750,18 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
     en.pairs = a.pairs;
     en.bbase = (int64_t)t * a.n_rs;
     en.own0 = (int)v_own0;
-    en.j0 = 0;
-    en.j1 = n_st;
+    en.j0 = split < 0 || part == 0 ? 0 : n_st / 2;
+    en.j1 = split < 0 || part == 1 ? n_st : n_st / 2;
     float e_acc = 0.f, posz = 0.f;
     en.run(eop, acc, e_acc, posz, nullptr);
+  }
+  if (split >= 0) {
+    float* __restrict__ tp = a.tailpart + ((int64_t)(split * 2 + part) * IW + wave * 32) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tp[acc_pos(i, lane / 32) * D + db * 32 + lane % 32] = acc[db][i];
+    return;
   }
 
   // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d])
@@ -758,6 +777,22 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
       const int64_t v = v_own0 + acc_pos(i, lane / 32);
       if (v < a.V) dE[v * D + d] = (T)(scf * (acc[db][i] + half));
     }
+  }
+}
+
+// dE of the halved tiles: the two partial sums added in a fixed order, then scaled as in k_items.
+template <typename T, int IW, int D>
+__global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
+  const int split = blockIdx.x;
+  const int64_t v0 = (int64_t)(a.n_full + split) * IW;
+  const float scf = (float)(a.ctl->scale * (double)a.grad_loss[0]);
+  const float* __restrict__ p0 = a.tailpart + (int64_t)(split * 2) * IW * D;
+  const float* __restrict__ p1 = p0 + (int64_t)IW * D;
+  T* __restrict__ dE = (T*)a.dE;
+  for (int e = threadIdx.x; e < IW * D; e += 256) {
+    const int64_t v = v0 + e / D;
+    const int d = e % D;
+    if (v < a.V) dE[v * D + d] = (T)(scf * ((p0[e] + p1[e]) + (float)(0.5 * a.sumH[d])));
   }
 }
 
@@ -831,7 +866,23 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   auto kern = k_items<T, D, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)L.n_vt), dim3(NW * 64), sm, st, a);
+  // P workgroups run at once; when the last round would be at most half full, its tiles are halved. The
+  // partial sums go to the forward sweep's dH partial area, which is not in use during the backward dE sweep
+  // (it holds at least 1024 tiles' worth of rows x D floats; P <= 1024).
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, NW * 64, sm) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int64_t P = (int64_t)cu_count() * per_cu;
+  const int64_t rem = L.n_vt % P;
+  const int64_t n_split = (L.n_vt > P && rem > 0 && 2 * rem <= P) ? rem : 0;
+  a.n_full = (int)(L.n_vt - n_split);
+  a.tailpart = (float*)(ws + L.off_dhpart);
+  if (n_split * 2 > (L.part_rows / (NW * 32))) return hipErrorInvalidValue;  // cannot happen: P <= 1024
+  hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || n_split == 0) return e;
+  hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((unsigned)n_split), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
