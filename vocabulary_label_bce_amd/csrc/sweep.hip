@@ -780,20 +780,23 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   }
 }
 
-// dE of the halved tiles: the two partial sums added in a fixed order, then scaled as in k_items.
+// dE of the halved tiles: the two partial sums added in a fixed order, then scaled as in k_items. Grid:
+// (halved tile, chunk of 1024 consecutive values); each thread handles 4 consecutive d of one item.
 template <typename T, int IW, int D>
 __global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
-  const int split = blockIdx.x;
-  const int64_t v0 = (int64_t)(a.n_full + split) * IW;
+  static_assert(D % 4 == 0 && (IW * D) % 1024 == 0, "tail chunking");
+  const int split = blockIdx.y;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // first value of this thread within the tile
+  const int64_t v = (int64_t)(a.n_full + split) * IW + e / D;
+  if (v >= a.V) return;
+  const int d = e % D;
   const float scf = (float)(a.ctl->scale * (double)a.grad_loss[0]);
-  const float* __restrict__ p0 = a.tailpart + (int64_t)(split * 2) * IW * D;
-  const float* __restrict__ p1 = p0 + (int64_t)IW * D;
-  T* __restrict__ dE = (T*)a.dE;
-  for (int e = threadIdx.x; e < IW * D; e += 256) {
-    const int64_t v = v0 + e / D;
-    const int d = e % D;
-    if (v < a.V) dE[v * D + d] = (T)(scf * ((p0[e] + p1[e]) + (float)(0.5 * a.sumH[d])));
-  }
+  const float4 p0 = *(const float4*)(a.tailpart + (int64_t)(split * 2) * IW * D + e);
+  const float4 p1 = *(const float4*)(a.tailpart + (int64_t)(split * 2 + 1) * IW * D + e);
+  const float q[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+  T* __restrict__ out = (T*)a.dE + v * D + d;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = (T)(scf * (q[k] + (float)(0.5 * a.sumH[d + k])));
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -882,7 +885,8 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || n_split == 0) return e;
-  hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((unsigned)n_split), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((NW * 32 * D) / 1024, (unsigned)n_split), dim3(256), 0, st,
+                     a);
   return hipGetLastError();
 }
 
