@@ -291,11 +291,14 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // streamed matrix X (E or Hc) and its slot-packed copy Xsp flow through the LDS rings.
 //   FWD: epilogue = softplus (+ sigma with GRAD), owner = rows; !FWD: epilogue = sigma, owner = items.
 // Runs steps [j0, j1) of 32 streamed rows; bucket pointers of step j are bptr[bbase + j], bptr[bbase + j + 1].
-// Iteration i issues the logit GEMM of step i+1 and the gradient GEMM of step i-1 (with the G of step i-1,
-// packed at the end of iteration i-1) and evaluates the epilogue of step i; none of the three depends on
-// another inside the iteration. Ring schedule (step j, ring depth N): its d-packed block is loaded at
-// iteration j - N into slot j % N and read at iteration j - 1; its slot-packed block is loaded at iteration
-// j - N + 2 into slot j % N and read at iteration j + 1. One barrier starts every iteration.
+// Two schedules, both with the gradient GEMM of step i-1 (on the G tile packed in iteration i-1) in iteration i:
+//  - kPrefetch (the A operands of a step fit in 32 registers per lane: bf16 D <= 128, f32 D <= 64): iteration
+//    i runs the logit GEMM of step i on A operands read from LDS during iteration i-1, reads those of step
+//    i+1, and evaluates the epilogue of step i;
+//  - otherwise the logit GEMM of step i+1 runs in iteration i with its A operands read next to each MFMA, two
+//    logit tiles alternating, and the epilogue of step i uses the tile formed in iteration i-1.
+// Ring loads, their slots and the barrier every kK iterations follow Geo; bucket pointers come 64 steps at a
+// time (bkt_*), their refill riding on a barrier iteration.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int KT = 0>
 struct Engine {
@@ -401,12 +404,12 @@ struct Engine {
   // Runs the sweep; `own` holds the owner operand for every k-step. On return acc holds the gradient tile
   // (GRAD) and e_acc / posz the forward row sums (FWD).
   //
-  // Iteration i does the logit GEMM of step i and the gradient GEMM of step i-1 (with the G tile of step i-1)
-  // on the matrix cores, then reads the A operands of step i+1 and runs the epilogue of step i (giving G(i))
-  // on the vector ALU; none of these depends on another inside the iteration. Each wave keeps one logit tile,
-  // one G tile and the A operands of its next logit GEMM in registers. Barriers come only every kK
-  // iterations, so the waves of a SIMD drift apart and one wave's vector work overlaps another's MFMAs. A last
-  // iteration i = n finishes the pipeline (no loads, no logit GEMM).
+  // Prefetching schedule: iteration i does the logit GEMM of step i and the gradient GEMM of step i-1 (with the
+  // G tile of step i-1) on the matrix cores, reads the A operands of step i+1, and runs the epilogue of step i
+  // (giving G(i)) on the vector ALU. Only the epilogue depends on another of these (the logit GEMM), so the
+  // gradient MFMAs interleave with it, and the scalar work of the ring loads fills the gaps of the logit
+  // GEMM's dependent MFMA chain. Each wave keeps one logit tile, one G tile and the A operands of its next
+  // logit GEMM in registers. A last iteration i = n finishes the pipeline (no loads, no logit GEMM).
   __device__ inline void run(const Op* own, f32x16* acc, float& e_acc, float& posz, int* met,
                              TopK<KT ? KT : 1>* tk = nullptr) {
     const int n = j1 - j0;

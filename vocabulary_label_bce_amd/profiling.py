@@ -27,13 +27,21 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 SWEEP_SOURCES = ("common.h", "sweep.hip")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with runs of whitespace collapsed, so that edits to comments alone do
+    not mark measured counters as stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """sha256 over the sources of the sweep kernels (file names and contents)."""
+    """sha256 over the code of the sweep kernels' sources (file names and comment-free contents)."""
     h = hashlib.sha256()
     for f in SWEEP_SOURCES:
         h.update(f.encode())
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
