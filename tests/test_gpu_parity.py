@@ -271,3 +271,57 @@ def test_malformed_offsets_are_clamped():
     pb = dict(p)
     pb["row_offsets"] = torch.from_numpy(bad.astype(np.int32))
     _check(p, _run(pb, g=1.0), ref)
+
+
+def test_positives_at_bucket_block_boundaries():
+    """Bucket pointers reach a wave 64 steps at a time, the next block being loaded at steps 64, 128, ... of a
+    unit. 65,536 valid rows make 256 row tiles, so the forward sweep runs one vocabulary split and each unit
+    spans all 136 item steps; the dE sweep spans 2,048 row steps. Positives are planted at the last and first
+    steps of the blocks (item steps 63, 64, 65, 127, 128; all rows of row steps 62-66, 126-130, 190-194).
+    Sampled rows and items against the oracle."""
+    R, V, D = 65536, 4200, 64
+    rng = np.random.default_rng(31)
+    counts = rng.integers(1, 4, size=R)
+    rows = np.repeat(np.arange(R), counts)
+    items = rng.integers(0, V, size=rows.size)
+    plant_rows = np.array([0, 1, 2047, 2048, 4095, 4096, 30000, R - 1])
+    plant_items = np.array([63 * 32 + 5, 64 * 32, 64 * 32 + 31, 65 * 32 + 7, 127 * 32 + 17, 128 * 32 + 2, V - 1])
+    check_items = np.array([5, 2048, 4100, V - 1])
+    # every row of the row steps around 64, 128 and 192: a block read from the wrong place moves dE of these
+    # items by several times the tolerance
+    step_rows = np.concatenate([np.arange(32 * s0, 32 * (s0 + 5)) for s0 in (62, 126, 190)])
+    extra_r = np.concatenate([np.repeat(plant_rows, plant_items.size), np.repeat(step_rows, check_items.size)])
+    extra_i = np.concatenate([np.tile(plant_items, plant_rows.size), np.tile(check_items, step_rows.size)])
+    rows = np.concatenate([rows, extra_r])
+    items = np.concatenate([items, extra_i])
+    order = np.argsort(rows, kind="stable")
+    rows, items = rows[order], items[order]
+    ro = np.zeros(R + 1, np.int32)
+    np.cumsum(np.bincount(rows, minlength=R), out=ro[1:])
+    gen = torch.Generator().manual_seed(31)
+    H = 0.4 * torch.randn(R, D, generator=gen)
+    E = 0.4 * torch.randn(V, D, generator=gen)
+    # the planted rows share one H row and the checked items have small embeddings, so the planted positives
+    # dominate those items' dE: dropping one region of them moves it by ~27x the tolerance (oracle, on the CPU)
+    H[torch.from_numpy(step_rows)] = 0.4 * torch.randn(D, generator=gen)
+    E[torch.from_numpy(check_items)] = 0.01 * torch.randn(check_items.size, D, generator=gen)
+    H, E = H.to(torch.bfloat16), E.to(torch.bfloat16)
+    cpu = dict(H=H, E=E, row_offsets=torch.from_numpy(ro), item_ids=torch.from_numpy(items.astype(np.int32)),
+               row_mask=torch.ones(R, dtype=torch.uint8))
+    p = _dev(cpu)
+    w = Workspace(p["H"], p["E"], p["item_ids"], want_row_loss=True, save_dh=True)
+    g = torch.tensor([1.0], device="cuda")
+    w.forward(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"])
+    dH, dE = w.backward(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], grad=g)
+    torch.cuda.synchronize()
+    srows = np.unique(np.concatenate([plant_rows, step_rows[::37], rng.choice(R, size=8, replace=False)]))
+    sitems = np.unique(np.concatenate([plant_items, check_items, rng.choice(V, size=8, replace=False)]))
+    ref_r = oracle.rows(cpu["H"], cpu["E"], cpu["row_offsets"], cpu["item_ids"], cpu["row_mask"], srows)
+    ref_i = oracle.items(cpu["H"], cpu["E"], cpu["row_offsets"], cpu["item_ids"], cpu["row_mask"], sitems)
+    tol = TOL[torch.bfloat16]
+    rl = w.row_loss.double().cpu().numpy()[srows]
+    np.testing.assert_allclose(rl, ref_r["row_loss"], rtol=tol["row"], atol=tol["row"] * np.abs(ref_r["row_loss"]).max())
+    got_dH = dH.double().cpu().numpy()[srows]
+    assert np.abs(got_dH - ref_r["dH"]).max() <= tol["grad"] * np.abs(ref_r["dH"]).max()
+    got_dE = dE.double().cpu().numpy()[sitems]
+    assert np.abs(got_dE - ref_i["dE"]).max() <= tol["grad"] * np.abs(ref_i["dE"]).max()
