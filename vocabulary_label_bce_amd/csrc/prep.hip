@@ -21,6 +21,12 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
+// Plain int copy as a kernel (a kernel node when the caller captures the stream into a graph).
+__global__ void k_copy_i32(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -392,8 +398,10 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   }
   if ((e = scan_exclusive(bptr, nb, (int32_t*)(ws + L.off_scan), st)) != hipSuccess) return e;
   if (L.nnz > 0) {
-    if ((e = hipMemcpyAsync(bfill, bptr, nb * sizeof(int32_t), hipMemcpyDeviceToDevice, st)) != hipSuccess)
-      return e;
+    int64_t cblocks = (nb + 255) / 256;
+    if (cblocks > 65536) cblocks = 65536;
+    hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cblocks), dim3(256), 0, st, bfill, (const int32_t*)bptr, nb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
                        (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bfill, pairs,
                        (int*)nullptr);

@@ -22,6 +22,8 @@
 //
 // The forward sweep also serves full-vocabulary scoring (top-k per row, Section I-E's evaluation) with a
 // running top list per lane in place of the loss epilogue, and can count the Cut Metrics of Section III-D.
+#include <atomic>
+
 #include "common.h"
 
 namespace cutbce {
@@ -805,16 +807,37 @@ __global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
 // ---------------------------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------------------------
-static int g_cus = 0;
+constexpr int kMaxDevices = 16;  // devices whose launch data is cached (others query every time)
+
+// Compute units of the current device, cached per device.
 static int cu_count() {
-  if (g_cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    g_cus = n;
-  }
-  return g_cus;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const int slot = dev >= 0 && dev < kMaxDevices ? dev : -1;
+  int n = slot >= 0 ? cached[slot].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (slot >= 0) cached[slot].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Once per kernel and device: the dynamic-LDS limit and the number of workgroups resident per CU (both fixed
+// for a kernel). Later launches then make no runtime call but the launch itself, which also keeps them
+// capturable into a graph.
+template <auto Kern>
+static hipError_t kernel_setup(int threads, size_t sm, int& per_cu) {
+  static std::atomic<int> cached[kMaxDevices];  // resident workgroups per CU; 0 = not set up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0 && (per_cu = cached[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)Kern, threads, sm) != hipSuccess || n < 1) n = 1;
+  per_cu = n;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return hipSuccess;
 }
 
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT = 0>
@@ -839,14 +862,11 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   a.topv = (float*)(ws + L.off_dhpart);
   a.topi = (int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * (KT ? KT : 1);
   const size_t sm = G::kLdsBytes;
-  auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-  if (e != hipSuccess) return e;
+  constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
   // persistent: as many workgroups as can be resident at once, a multiple of 8 (one range per XCD)
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, NW * 64, sm) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
+  int per_cu = 1;
+  hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
+  if (e != hipSuccess) return e;
   const int P = (cu_count() * per_cu / 8) * 8;
   hipLaunchKernelGGL(kern, dim3(P > 0 ? P : 8), dim3(NW * 64), sm, st, a);
   return hipGetLastError();
@@ -869,16 +889,13 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   a.V = L.V;
   a.n_rs = L.n_rs;
   const size_t sm = G::kLdsBytes;
-  auto kern = k_items<T, D, NW>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  constexpr auto kern = k_items<T, D, NW>;
+  int per_cu = 1;
+  hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
   if (e != hipSuccess) return e;
   // P workgroups run at once; when the last round would be at most half full, its tiles are halved. The
   // partial sums go to the forward sweep's dH partial area, which is not in use during the backward dE sweep
   // (it holds at least 1024 tiles' worth of rows x D floats; P <= 1024).
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, NW * 64, sm) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
   const int64_t P = (int64_t)cu_count() * per_cu;
   const int64_t rem = L.n_vt % P;
   const int64_t n_split = (L.n_vt > P && rem > 0 && 2 * rem <= P) ? rem : 0;
