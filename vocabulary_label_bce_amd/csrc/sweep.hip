@@ -158,9 +158,8 @@ struct TopK {
 // The streamed operand moves through two LDS rings, one 32-row block per step: the d-packed block of step j
 // (A, read for the logit GEMM during iteration j - 1) and its slot-packed copy (B, read by the gradient GEMM
 // during iteration j + 1). Workgroup barriers come every kK iterations (at iterations that are multiples of
-// kK), so that between two barriers the waves drift apart freely and one wave's vector work overlaps
-// another's MFMAs. With kS = 1 a barrier waits for all loads but those issued in the iteration just before
-// it. Then:
+// kK): a barrier costs a wait of every wave for the slowest, and kK = 2 at 8 KB steps measured best. With
+// kS = 1 a barrier waits for all loads but those issued in the iteration just before it. Then:
 //   A(j) is loaded at iteration j - kLA into slot j % kNA; B(j) at iteration j - kLB into slot j % kNB, with
 //   kLA >= kK + 1 + kS, kLB >= kK - 1 + kS     (a barrier separates landing from reading),
 //   kNA >= kLA + kK - 1, kNB >= kLB + kK + 1     (a barrier separates the last read of a slot from its
