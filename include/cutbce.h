@@ -35,6 +35,9 @@
  *     floating-point atomics).
  *   - The workspace is scratch: its contents on entry are ignored and on return are unspecified. Concurrent
  *     calls must use distinct workspaces.
+ *   - The first compute call of a problem type on a device also sets up per-kernel launch data (dynamic LDS
+ *     limit, resident workgroups per CU). Later calls enqueue kernel launches only (no memset or memcpy), so a
+ *     caller can capture them into a HIP graph and replay it; the replays read the inputs anew.
  */
 #ifndef CUTBCE_H
 #define CUTBCE_H
