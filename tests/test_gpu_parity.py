@@ -127,15 +127,17 @@ def test_smallest_shapes(R, V, dtype):
     _check(p, _run(p, g=1.0), ref, excess=False)
 
 
-@pytest.mark.parametrize("dtype,tile", [("bf16", 256), ("f32", 128)])
-def test_halved_tail_tiles_of_the_de_sweep(dtype, tile):
+@pytest.mark.parametrize("dtype,tile,D,rounds", [("bf16", 256, 128, 1), ("f32", 128, 128, 1), ("f32", 128, 256, 2)])
+def test_halved_tail_tiles_of_the_de_sweep(dtype, tile, D, rounds):
     """More item tiles than workgroups that run at once, with a remainder of at most half a round: the last
     tiles are swept in two row halves whose partial sums a finishing kernel adds. At D = 128 one workgroup
-    fits per compute unit, so the remainder is CUs / 4 tiles. Full dE against the oracle."""
+    fits per compute unit, so the remainder is CUs / 4 tiles. f32 D = 256 runs the sweep as two passes over
+    halves of dE's columns; 2 CUs + CUs / 4 tiles leave a remainder of CUs / 4 whether one or two workgroups fit
+    per compute unit. Full dE against the oracle."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    n_tiles = cus + cus // 4
+    n_tiles = rounds * cus + cus // 4
     V = n_tiles * tile - 37  # ragged last tile
-    p = W.custom_problem(40, V, 128, dtype=dtype, seed=21, h_std=0.3, e_std=0.3, pos_per_row=(1, 16),
+    p = W.custom_problem(40, V, D, dtype=dtype, seed=21, h_std=0.3, e_std=0.3, pos_per_row=(1, 16),
                          mask_frac=0.2)
     ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.75)
     _check(p, _run(p, g=0.75), ref)

@@ -223,7 +223,7 @@ __device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int
 // e_acc gathers the bracket (it is 0 for z = 0, so zero padding adds nothing), 16 logits at a time as
 // sum|z|/2 + ln 2 * (log2(prod(1 + e^-|z|)) - 16); z/2 and ln 2 are added back per row in float64.
 // With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives) = sign(z) (1/(1+e^-|z|) - 1/2).
-template <bool GRAD, bool HASPOS>
+template <bool GRAD, bool HASPOS, bool LOSS = true>
 __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e_acc, float& posz) {
   // u_i = -|z_i| log2(e); w_i = 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow. The
   // product is formed over adjacent pairs, then quads, then the whole tile (the sum of u alongside).
@@ -257,10 +257,12 @@ __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e
       for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(r[k] - 0.5f, z[4 * q + k]);
     }
   }
-  const float wp = (w4[0] * w4[1]) * (w4[2] * w4[3]);
-  const float up = (u4[0] + u4[1]) + (u4[2] + u4[3]);
-  // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2] = ln 2 * (log2(prod) - 16 - sum_i u_i / 2)
-  e_acc += kLn2 * (__builtin_amdgcn_logf(wp) - 16.f - 0.5f * up);
+  if (LOSS) {
+    const float wp = (w4[0] * w4[1]) * (w4[2] * w4[3]);
+    const float up = (u4[0] + u4[1]) + (u4[2] + u4[3]);
+    // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2] = ln 2 * (log2(prod) - 16 - sum_i u_i / 2)
+    e_acc += kLn2 * (__builtin_amdgcn_logf(wp) - 16.f - 0.5f * up);
+  }
   if (HASPOS) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -301,7 +303,10 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // Ring loads, their slots and the barrier every kK iterations follow Geo; bucket pointers come 64 steps at a
 // time (bkt_*), their refill riding on a barrier iteration.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int KT = 0>
+// DB0, NDBE: the gradient GEMM covers the d-blocks [DB0, DB0 + NDBE) of the 32-wide blocks of D (acc holds
+// NDBE tiles); LOSS = false skips the loss sums of the forward epilogue (a second pass over the other d-blocks).
+template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int KT = 0, int DB0 = 0,
+          int NDBE = D / 32, bool LOSS = true>
 struct Engine {
   using EL = Elem<T>;
   using G = Geo<T, D, NW, GRAD>;
@@ -519,9 +524,10 @@ struct Engine {
   __device__ inline void grad_slot(int slot, const GPack<T>& g, f32x16* acc) const {
     const char* b = lds + (G::kNA + slot) * G::kStepBytes;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDBE; ++db)
 #pragma unroll
-      for (int q = 0; q < EL::kGroups; ++q) acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, db, q, lane), acc[db]);
+      for (int q = 0; q < EL::kGroups; ++q)
+        acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, DB0 + db, q, lane), acc[db]);
   }
 
   // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step (bucket [pb, pe)),
@@ -552,7 +558,7 @@ struct Engine {
     }
     float c[16];
     if (FWD)
-      epi_rows<GRAD, false>(z, 0u, c, e_acc, posz);
+      epi_rows<GRAD, false, LOSS>(z, 0u, c, e_acc, posz);
     else
       epi_items<false>(z, 0u, c);
     if (MET) {
@@ -601,11 +607,15 @@ struct RowsArgs {
 // row tile t) are assigned in contiguous per-XCD ranges so that the workgroups sharing an L2 stream the same
 // part of E. With KT > 0 it scores instead: per-lane top-KT lists, merged per row and written per unit.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT>
+// DHPART 0: one pass (loss, dH and optional Cut Metrics); 1 / 2: the first / second of two passes, each
+// accumulating half of dH's d-blocks (half the accumulator registers, for D = 512); the loss and the Cut
+// Metrics come from pass 1.
+template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT, int DHPART = 0>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   using EL = Elem<T>;
-  using EN = Engine<T, D, NW, true, WITH_DH, MET, KT>;
-  constexpr int RW = NW * 32, KS = D / EL::kK, NDB = D / 32;
+  constexpr int NDB = D / 32, NDBE = DHPART ? NDB / 2 : NDB, DB0 = DHPART == 2 ? NDB / 2 : 0;
+  using EN = Engine<T, D, NW, true, WITH_DH, MET, KT, DB0, NDBE, DHPART != 2>;
+  constexpr int RW = NW * 32, KS = D / EL::kK;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   const T* __restrict__ Hc = (const T*)a.Hc;
@@ -642,9 +652,9 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       hop[ks] = load_op<T>(Hc + (int64_t)(r_base + lane % 32) * D + ks * EL::kK + (lane / 32) * EL::kEPL);
-    f32x16 acc[WITH_DH ? NDB : 1];
+    f32x16 acc[WITH_DH ? NDBE : 1];
 #pragma unroll
-    for (int db = 0; db < (WITH_DH ? NDB : 1); ++db) acc[db] = f32x16{};
+    for (int db = 0; db < (WITH_DH ? NDBE : 1); ++db) acc[db] = f32x16{};
     float e_acc = 0.f, posz = 0.f;
     int met[3] = {0, 0, 0};
     TopK<KT ? KT : 1> tk;
@@ -675,9 +685,11 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
       }
       continue;
     }
-    const float e_tot = e_acc + __shfl_xor(e_acc, 32, 64);
-    const float p_tot = posz + __shfl_xor(posz, 32, 64);
-    if (lane < 32) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    if (DHPART != 2) {
+      const float e_tot = e_acc + __shfl_xor(e_acc, 32, 64);
+      const float p_tot = posz + __shfl_xor(posz, 32, 64);
+      if (lane < 32) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    }
     if (MET) {
 #pragma unroll
       for (int q = 0; q < 3; ++q) met[q] += __shfl_xor(met[q], 32, 64);
@@ -685,10 +697,10 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     }
     if (WITH_DH) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDBE; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          a.dhpart[(urow + acc_pos(i, lane / 32)) * D + db * 32 + lane % 32] = acc[db][i];
+          a.dhpart[(urow + acc_pos(i, lane / 32)) * D + (DB0 + db) * 32 + lane % 32] = acc[db][i];
     }
   }
 }
@@ -711,11 +723,14 @@ struct ItemsArgs {
 // ---------------------------------------------------------------------------------------------------------
 // Backward dE sweep: workgroup = item tile (32 items per wave), sweeping all valid rows.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D, int NW>
+// DEPART 0: one pass; 1 / 2: the first / second of two passes, each accumulating and writing half of dE's
+// d-blocks (half the accumulator registers, for D = 512).
+template <typename T, int D, int NW, int DEPART = 0>
 __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   using EL = Elem<T>;
-  using EN = Engine<T, D, NW, false, true>;
-  constexpr int IW = NW * 32, KS = D / EL::kK, NDB = D / 32;
+  constexpr int NDB = D / 32, NDBE = DEPART ? NDB / 2 : NDB, DB0 = DEPART == 2 ? NDB / 2 : 0;
+  using EN = Engine<T, D, NW, false, true, false, 0, DB0, NDBE>;
+  constexpr int IW = NW * 32, KS = D / EL::kK;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   const T* __restrict__ E = (const T*)a.E;
@@ -738,9 +753,9 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
       eop[ks] = typename EL::Op{};
     }
   }
-  f32x16 acc[NDB];
+  f32x16 acc[NDBE];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < NDBE; ++db) acc[db] = f32x16{};
 
   const int n_valid = a.ctl->n_valid;
   const int n_st = (n_valid + 31) / 32;
@@ -762,9 +777,9 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   if (split >= 0) {
     float* __restrict__ tp = a.tailpart + ((int64_t)(split * 2 + part) * IW + wave * 32) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDBE; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tp[acc_pos(i, lane / 32) * D + db * 32 + lane % 32] = acc[db][i];
+      for (int i = 0; i < 16; ++i) tp[acc_pos(i, lane / 32) * D + (DB0 + db) * 32 + lane % 32] = acc[db][i];
     return;
   }
 
@@ -773,8 +788,8 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   const float scf = (float)sc;
   T* __restrict__ dE = (T*)a.dE;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = db * 32 + lane % 32;
+  for (int db = 0; db < NDBE; ++db) {
+    const int d = (DB0 + db) * 32 + lane % 32;
     const float half = (float)(0.5 * a.sumH[d]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -839,6 +854,22 @@ static hipError_t kernel_setup(int threads, size_t sm, int& per_cu) {
   return hipSuccess;
 }
 
+// Gradient accumulators (NDB tiles of 16 registers) plus the owner operand (D / k-per-MFMA operands) per lane:
+// when they fill the 256 registers of a wave, the sweep can run as two passes over half of the gradient's
+// d-blocks each (bf16 D = 512, f32 D = 256), recomputing the logits instead of spilling. Measured, forward:
+// bf16 D = 512 4.95 -> 2.47 ms, f32 D = 256 26.4 -> 17.2 ms (4,096 rows, 131,072 items).
+template <typename T, int D>
+constexpr bool two_pass() {
+  return (D / 32) * 16 + (D / Elem<T>::kK) * (int)(sizeof(typename Elem<T>::Op) / 4) >= 256;
+}
+
+// Forward-sweep grid: persistent, as many workgroups as can be resident at once (per_cu per CU), a multiple of
+// 8 (one range per XCD). The kernel derives its vocabulary splits from the grid size.
+static int persistent_grid(int per_cu) {
+  const int P = (cu_count() * per_cu / 8) * 8;
+  return P > 0 ? P : 8;
+}
+
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT = 0>
 static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st) {
   using G = Geo<T, D, NW, WITH_DH>;
@@ -861,14 +892,28 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   a.topv = (float*)(ws + L.off_dhpart);
   a.topi = (int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * (KT ? KT : 1);
   const size_t sm = G::kLdsBytes;
-  constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
-  // persistent: as many workgroups as can be resident at once, a multiple of 8 (one range per XCD)
-  int per_cu = 1;
-  hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
-  if (e != hipSuccess) return e;
-  const int P = (cu_count() * per_cu / 8) * 8;
-  hipLaunchKernelGGL(kern, dim3(P > 0 ? P : 8), dim3(NW * 64), sm, st, a);
-  return hipGetLastError();
+  // Both passes run on the same grid, hence the same vocabulary splits and partial-sum layout.
+  constexpr bool kTwoPass = WITH_DH && KT == 0 && two_pass<T, D>();
+  if constexpr (kTwoPass) {
+    constexpr auto k1 = k_rows<T, D, NW, WITH_DH, MET, KT, 1>;
+    constexpr auto k2 = k_rows<T, D, NW, WITH_DH, false, KT, 2>;
+    int c1 = 1, c2 = 1;
+    hipError_t e = kernel_setup<k1>(NW * 64, sm, c1);
+    if (e != hipSuccess) return e;
+    if ((e = kernel_setup<k2>(NW * 64, sm, c2)) != hipSuccess) return e;
+    const int P = persistent_grid(c1 < c2 ? c1 : c2);
+    hipLaunchKernelGGL(k1, dim3(P), dim3(NW * 64), sm, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k2, dim3(P), dim3(NW * 64), sm, st, a);
+    return hipGetLastError();
+  } else {
+    constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
+    int per_cu = 1;
+    hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm, st, a);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int D, int NW>
@@ -888,10 +933,19 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   a.V = L.V;
   a.n_rs = L.n_rs;
   const size_t sm = G::kLdsBytes;
-  constexpr auto kern = k_items<T, D, NW>;
+  // Two passes (see two_pass) run on the same grid and tail split. Measured: f32 D = 256 (the single pass
+  // spills ~300 registers) 8.3 vs 21 ms; bf16 D = 512 (~100 spilled) is faster in one pass, 1.87 vs 2.03 ms.
+  constexpr bool kTwoPass = two_pass<T, D>() && sizeof(T) == 4;
+  constexpr auto kern = k_items<T, D, NW, kTwoPass ? 1 : 0>;
+  constexpr auto kern2 = k_items<T, D, NW, kTwoPass ? 2 : 0>;
   int per_cu = 1;
   hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
   if (e != hipSuccess) return e;
+  if (kTwoPass) {
+    int c2 = 1;
+    if ((e = kernel_setup<kern2>(NW * 64, sm, c2)) != hipSuccess) return e;
+    if (c2 < per_cu) per_cu = c2;
+  }
   // P workgroups run at once; when the last round would be at most half full, its tiles are halved. The
   // partial sums go to the forward sweep's dH partial area, which is not in use during the backward dE sweep
   // (it holds at least 1024 tiles' worth of rows x D floats; P <= 1024).
@@ -903,6 +957,10 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   if (n_split * 2 > (L.part_rows / (NW * 32))) return hipErrorInvalidValue;  // cannot happen: P <= 1024
   hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
   e = hipGetLastError();
+  if (e == hipSuccess && kTwoPass) {
+    hipLaunchKernelGGL(kern2, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || n_split == 0) return e;
   hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((NW * 32 * D) / 1024, (unsigned)n_split), dim3(256), 0, st,
                      a);
