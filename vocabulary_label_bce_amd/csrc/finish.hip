@@ -2,10 +2,10 @@
 // the loss, the per-row losses and dH, and the cotangent scaling of dH in the backward.
 //
 // Per valid row r the forward sweep leaves, for every vocabulary split, (e, p): e = sum over the split's items
-// of softplus(z) - ln 2 - z/2 and p = sum of z over the row's positives in the split. With the row's logit sum
+// of softplus(z) - ln 2 - z and p = sum of z over the row's positives in the split. With the row's logit sum
 // sum_v z_rv = H[r] . (sum_v E[v]) (a rank-1 identity, evaluated in float64), the unnormalised row loss of
 // "Cut Binary Cross Entropy" Eq. (2)-(3) is
-//   V ln 2 + (1/2) H[r].sum_v E[v] + sum_splits e - sum_splits p,
+//   V ln 2 + H[r].sum_v E[v] + sum_splits e - sum_splits p,
 // and dH[r] = s * (sum_splits dH_part + (1/2) sum_v E[v]) (Eq. (4) with sigma split as (sigma - 1/2) + 1/2).
 // With Cut Metrics (Section III-D) the sweep also leaves, per split, the counts of logits predicted positive
 // (z > 0), of positives predicted positive and of positives; TP, FP, FN and TN follow by subtraction.
@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
     const int fp = np - tp, fn = npos - tp, tn = (int)(V - tp - fp - fn);
     if (lane < 4) metrics[r * 4 + lane] = lane == 0 ? tp : lane == 1 ? fp : lane == 2 ? fn : tn;
   }
-  const double rl = (double)V * 0.69314718055994530942 + 0.5 * zs + e - p;
+  const double rl = (double)V * 0.69314718055994530942 + zs + e - p;
   if (lane == 0) {
     if (row_loss) row_loss[r] = (float)rl;
     rowloss_c[k] = rl;

@@ -218,51 +218,83 @@ __device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int
   return load_op<T>((const T*)blk + slot_off<T>(D, db, g, lane));
 }
 
-// Epilogue of the forward sweep for one 32x32 tile (16 values per lane). With
-//   softplus(z) = max(z,0) + ln(1 + e^-|z|) = ln 2 + z/2 + [ |z|/2 + ln((1 + e^-|z|) / 2) ],
+// Epilogue of the forward sweep for one 32x32 tile (16 values per lane). With t = e^-z and w = 1 + t,
+//   softplus(z) = ln 2 + z + [ln w - ln 2]   and   sigma(z) = 1/w,
 // e_acc gathers the bracket (it is 0 for z = 0, so zero padding adds nothing), 16 logits at a time as
-// sum|z|/2 + ln 2 * (log2(prod(1 + e^-|z|)) - 16); z/2 and ln 2 are added back per row in float64.
-// With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives) = sign(z) (1/(1+e^-|z|) - 1/2).
+// ln 2 * (log2(prod w) - 16); z and ln 2 are added back per row in float64 (sum_v z_rv = H[r] . sum_v E[v]).
+// With GRAD it also forms c = sigma(z) - 1/2 (minus 1 at positives).
+// w grows without bound for negative z, so this form holds while the tile's product of w stays below
+// kFastProd (then every partial product does too, and the reciprocal of each quad's product is a normal float).
+// A tile beyond it takes the |z| form instead, whose factors lie in (1, 2]:
+//   softplus(z) - z - ln 2 = [|z|/2 + ln((1 + e^-|z|) / 2)] - z/2,   c = sign(z) (1/(1 + e^-|z|) - 1/2).
+constexpr float kFastProd = 0x1p120f;
+
+// c_i = 1/w_i - 1/2 for 16 factors w_i >= 1 with pair products w2 and quad products w4 (each below 2^126):
+// one reciprocal per quad, then down the product tree (batch inversion): 1/(w0 w1) = w2 w3 / (w0 w1 w2 w3),
+// 1/w0 = w1 / (w0 w1), ...; each 1/w_i picks up two extra roundings.
+__device__ inline void inv_minus_half(const float* w, const float* w2, const float* w4, float* c) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float r4 = __builtin_amdgcn_rcpf(w4[q]);
+    const float ra = r4 * w2[2 * q + 1], rb = r4 * w2[2 * q];
+    c[4 * q] = ra * w[4 * q + 1] - 0.5f;
+    c[4 * q + 1] = ra * w[4 * q] - 0.5f;
+    c[4 * q + 2] = rb * w[4 * q + 3] - 0.5f;
+    c[4 * q + 3] = rb * w[4 * q + 2] - 0.5f;
+  }
+}
+
 template <bool GRAD, bool HASPOS, bool LOSS = true>
 __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e_acc, float& posz) {
-  // u_i = -|z_i| log2(e); w_i = 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow. The
-  // product is formed over adjacent pairs, then quads, then the whole tile (the sum of u alongside).
-  float u[16], w[16];
+  // The product is formed over adjacent pairs, then quads, then the whole tile.
+  float w[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    u[i] = __builtin_fabsf(z[i]) * -kLog2e;
-    w[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
-  }
-  float w2[8], w4[4], u2[8], u4[4];
+  for (int i = 0; i < 16; ++i) w[i] = 1.f + __builtin_amdgcn_exp2f(z[i] * -kLog2e);
+  float w2[8], w4[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w2[i] = w[2 * i] * w[2 * i + 1];
-    u2[i] = u[2 * i] + u[2 * i + 1];
-  }
+  for (int i = 0; i < 8; ++i) w2[i] = w[2 * i] * w[2 * i + 1];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w4[i] = w2[2 * i] * w2[2 * i + 1];
-    u4[i] = u2[2 * i] + u2[2 * i + 1];
-  }
-  if (GRAD) {
-    // 1/w_i from one reciprocal per quad (batch inversion down the product tree):
-    // 1/(w0 w1) = w2 w3 / (w0 w1 w2 w3), 1/w0 = w1 / (w0 w1), ...; each 1/w_i picks up two extra roundings.
-    // c_i = sigma(z_i) - 1/2 = sign(z_i) (1/w_i - 1/2).
+  for (int i = 0; i < 4; ++i) w4[i] = w2[2 * i] * w2[2 * i + 1];
+  const float wp = (w4[0] * w4[1]) * (w4[2] * w4[3]);
+  if (GRAD) inv_minus_half(w, w2, w4, c);
+  float e_inc = LOSS ? kLn2 * (__builtin_amdgcn_logf(wp) - 16.f) : 0.f;
+  // taken by the whole wave when any lane needs it (a branch around the rarely run code; all lanes may run it)
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(wp <= kFastProd)) != 0, 0)) {
+    // u_i = -|z_i| log2(e); wa_i = 1 + 2^u_i in (1, 2], so the product of 16 of them cannot overflow
+    float u[16], wa[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float r4 = __builtin_amdgcn_rcpf(w4[q]);
-      const float ra = r4 * w2[2 * q + 1], rb = r4 * w2[2 * q];
-      const float r[4] = {ra * w[4 * q + 1], ra * w[4 * q], rb * w[4 * q + 3], rb * w[4 * q + 2]};
+    for (int i = 0; i < 16; ++i) {
+      u[i] = __builtin_fabsf(z[i]) * -kLog2e;
+      wa[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
+    }
+    float a2[8], a4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(r[k] - 0.5f, z[4 * q + k]);
+    for (int i = 0; i < 8; ++i) a2[i] = wa[2 * i] * wa[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a4[i] = a2[2 * i] * a2[2 * i + 1];
+    if (GRAD) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float r4 = __builtin_amdgcn_rcpf(a4[q]);
+        const float ra = r4 * a2[2 * q + 1], rb = r4 * a2[2 * q];
+        const float r[4] = {ra * wa[4 * q + 1], ra * wa[4 * q], rb * wa[4 * q + 3], rb * wa[4 * q + 2]};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(r[k] - 0.5f, z[4 * q + k]);
+      }
+    }
+    if (LOSS) {
+      float us = 0.f, zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        us += u[i];
+        zs += z[i];
+      }
+      const float pa = (a4[0] * a4[1]) * (a4[2] * a4[3]);
+      // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2 - z_i / 2]
+      e_inc = kLn2 * (__builtin_amdgcn_logf(pa) - 16.f - 0.5f * us) - 0.5f * zs;
     }
   }
-  if (LOSS) {
-    const float wp = (w4[0] * w4[1]) * (w4[2] * w4[3]);
-    const float up = (u4[0] + u4[1]) + (u4[2] + u4[3]);
-    // sum_i [ln(1 + e^-|z_i|) - ln 2 + |z_i| / 2] = ln 2 * (log2(prod) - 16 - sum_i u_i / 2)
-    e_acc += kLn2 * (__builtin_amdgcn_logf(wp) - 16.f - 0.5f * up);
-  }
+  if (LOSS) e_acc += e_inc;
   if (HASPOS) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -274,7 +306,8 @@ __device__ inline void epi_rows(const f32x16& z, uint32_t pm, float* c, float& e
 }
 
 // Epilogue of the backward sweep: c = sigma(z) - 1/2 = 1/(1 + e^-z) - 1/2 (minus 1 at positives); e^-z may
-// overflow to +inf, which gives exactly -1/2.
+// overflow to +inf, which gives exactly -1/2. (Batch inversion as in the forward measured 6% slower here: the
+// product tree lengthens each lane's dependency chain more than the 12 saved reciprocals gain.)
 template <bool HASPOS>
 __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 #pragma unroll
