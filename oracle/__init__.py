@@ -50,9 +50,9 @@ def _load(plant: int = 0):
             return _libs[plant]
         lib = ctypes.CDLL(build(plant))
         i64, i32, f64, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
-        lib.oracle_rows.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp, vp]
-        lib.oracle_items.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
-        lib.oracle_full.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp, vp]
+        lib.oracle_rows.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, f64, i64, vp, vp, vp]
+        lib.oracle_items.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, f64, i64, vp, vp]
+        lib.oracle_full.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, f64, vp, vp, vp, vp]
         lib.oracle_metrics.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, f64, i64, vp, vp]
         lib.oracle_topk.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
         for f in (lib.oracle_rows, lib.oracle_items, lib.oracle_full, lib.oracle_metrics, lib.oracle_topk,
@@ -112,42 +112,63 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _weights(row_weight, R):
+    """float64 [R] row weights, or None (every valid row weighs 1)."""
+    if row_weight is None:
+        return None
+    if hasattr(row_weight, "detach"):
+        row_weight = row_weight.detach().cpu().double().numpy()
+    w = np.ascontiguousarray(np.asarray(row_weight, dtype=np.float64))
+    if w.shape != (R,):
+        raise ValueError(f"row_weight must have shape ({R},), got {w.shape}")
+    return w
+
+
 def _check(st):
     if st != 0:
         raise ValueError(f"oracle rejected the input: {ERRORS.get(st, st)}")
 
 
-def full(H, E, row_offsets, item_ids, row_mask, g: float = 1.0, grads: bool = True, plant: int = 0):
-    """Loss, per-row losses and (optionally) dH [R, D], dE [V, D], all float64 numpy."""
+def full(H, E, row_offsets, item_ids, row_mask, g: float = 1.0, grads: bool = True, plant: int = 0,
+         row_weight=None):
+    """Loss, per-row losses (unweighted) and (optionally) dH [R, D], dE [V, D], all float64 numpy.
+    row_weight: optional [R] weights of the rows (the weighted average of the C file's header)."""
     h, e, dt, R, V, D, ro, ids, m = _prep(H, E, row_offsets, item_ids, row_mask)
+    w = _weights(row_weight, R)
     loss = np.zeros(1, np.float64)
     rl = np.zeros(R, np.float64)
     dH = np.zeros((R, D), np.float64) if grads else None
     dE = np.zeros((V, D), np.float64) if grads else None
-    st = _load(plant).oracle_full(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m), float(g),
+    st = _load(plant).oracle_full(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m),
+                                  _ptr(w) if w is not None else None, float(g),
                                   _ptr(loss), _ptr(rl), _ptr(dH) if grads else None, _ptr(dE) if grads else None)
     _check(st)
     return dict(loss=float(loss[0]), row_loss=rl, dH=dH, dE=dE)
 
 
-def rows(H, E, row_offsets, item_ids, row_mask, rows, g: float = 1.0, grads: bool = True, plant: int = 0):
-    """Per-row loss (unnormalised) and dH rows for the listed rows only (s uses the full mask's R_v)."""
+def rows(H, E, row_offsets, item_ids, row_mask, rows, g: float = 1.0, grads: bool = True, plant: int = 0,
+         row_weight=None):
+    """Per-row loss (unnormalised) and dH rows for the listed rows only (s uses all valid rows)."""
     h, e, dt, R, V, D, ro, ids, m = _prep(H, E, row_offsets, item_ids, row_mask)
+    w = _weights(row_weight, R)
     rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     rl = np.zeros(rr.size, np.float64)
     dH = np.zeros((rr.size, D), np.float64) if grads else None
-    st = _load(plant).oracle_rows(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m), float(g),
+    st = _load(plant).oracle_rows(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m),
+                                  _ptr(w) if w is not None else None, float(g),
                                   rr.size, _ptr(rr), _ptr(rl), _ptr(dH) if grads else None)
     _check(st)
     return dict(row_loss=rl, dH=dH)
 
 
-def items(H, E, row_offsets, item_ids, row_mask, items, g: float = 1.0, plant: int = 0):
+def items(H, E, row_offsets, item_ids, row_mask, items, g: float = 1.0, plant: int = 0, row_weight=None):
     """dE rows for the listed items only."""
     h, e, dt, R, V, D, ro, ids, m = _prep(H, E, row_offsets, item_ids, row_mask)
+    w = _weights(row_weight, R)
     it = np.ascontiguousarray(np.asarray(items, dtype=np.int64))
     dE = np.zeros((it.size, D), np.float64)
-    st = _load(plant).oracle_items(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m), float(g),
+    st = _load(plant).oracle_items(R, V, D, dt, _ptr(h), _ptr(e), _ptr(ro), _ptr(ids), _ptr(m),
+                                   _ptr(w) if w is not None else None, float(g),
                                    it.size, _ptr(it), _ptr(dE))
     _check(st)
     return dict(dE=dE)

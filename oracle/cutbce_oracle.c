@@ -20,10 +20,15 @@
  * Readings where the paper is silent (each is listed in the design notes):
  *   - targets are given per row as a list of ids; y_rv = 1 iff v appears in row r's list (a repeated id
  *     counts once, since y is binary in Section III-A);
- *   - the per-position `weights` of the paper's API are read as a 0/1 row mask; positives of masked rows
- *     are ignored;
- *   - R_v = 0 (every row masked) gives loss 0 and zero gradients;
- *   - row_loss[r] is the unnormalised sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
+ *   - the per-position `weights` of the paper's API: a row mask (0 = padding, whose positives are ignored)
+ *     and, optionally, a weight w_r per row (1 when none is given). The average over positions becomes the
+ *     weighted average: with W = sum of w_r over valid rows and s = 1 / (W * V),
+ *       loss  = s * sum_{valid r} w_r sum_v L(z_rv, y_rv),
+ *       dH[r] = g * s * w_r * sum_v (sigma(z_rv) - y_rv) E[v],
+ *       dE[v] = g * s * sum_{valid r} w_r (sigma(z_rv) - y_rv) H[r];
+ *     unit weights give the plain average above (W = R_v);
+ *   - W = 0 (every row masked, or all weights 0) gives loss 0 and zero gradients;
+ *   - row_loss[r] is the unnormalised, unweighted sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
  *
  * Full-vocabulary top-k (Section I-E evaluation): per valid row, the k items with the largest logits, ordered
  * by logit (descending) and, among equal logits, by item id (ascending); Hit@k counts a row as a hit when at
@@ -85,6 +90,28 @@ static double sigmoid(double x) {
     return e / (1.0 + e);
 }
 
+/* Weight of row r: 0 for a masked row, else row_weight[r] (1 without weights). */
+static double row_w(const uint8_t *row_mask, const double *row_weight, int64_t r) {
+    if (!row_mask[r]) return 0.0;
+    return row_weight ? row_weight[r] : 1.0;
+}
+
+/* s = 1 / (W * V) with W the summed weight of the valid rows (rows in ascending order); 0 when W = 0. */
+static double norm_scale(int64_t R, int64_t V, const uint8_t *row_mask, const double *row_weight) {
+    double W = 0.0;
+    for (int64_t r = 0; r < R; ++r) {
+#if ORACLE_PLANT == 6
+        W += row_mask[r] ? 1.0 : 0.0; /* planted: the normaliser ignores the weights */
+#else
+        W += row_w(row_mask, row_weight, r);
+#endif
+    }
+#if ORACLE_PLANT == 2
+    W = (double)R; /* planted: padding rows counted in the average */
+#endif
+    return W != 0.0 ? 1.0 / (W * (double)V) : 0.0;
+}
+
 /* Check CSR consistency and id range; count valid rows. */
 static int check_inputs(int64_t R, int64_t V, int D, const int32_t *row_offsets, const int32_t *item_ids,
                         const uint8_t *row_mask, int64_t *n_valid) {
@@ -141,20 +168,18 @@ int oracle_num_threads(void) {
 
 /*
  * Row side: for each requested row (n_rows entries of `rows`; all R rows when rows == NULL) compute
- * row_loss[i] = sum_v L(z, y) (0 for a masked row) and, when dH != NULL, dH[i][:] = g*s*sum_v (sigma-y) E[v]
- * (0 for a masked row). s uses the global R_v of the full mask.
+ * row_loss[i] = sum_v L(z, y) (0 for a masked row) and, when dH != NULL,
+ * dH[i][:] = g*s*w_r*sum_v (sigma-y) E[v] (0 for a masked row). s uses the weight of all valid rows.
  */
 int oracle_rows(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
-                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
-                int64_t n_rows, const int64_t *rows, double *row_loss, double *dH) {
+                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                const double *row_weight, double g, int64_t n_rows, const int64_t *rows, double *row_loss,
+                double *dH) {
     int64_t rv;
     int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
     if (st) return st;
     if (!rows) n_rows = R;
-    double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
-#if ORACLE_PLANT == 2
-    s = 1.0 / ((double)R * (double)V); /* planted: padding rows counted in the average */
-#endif
+    const double s = norm_scale(R, V, row_mask, row_weight);
     int err = 0;
 #pragma omp parallel
     {
@@ -200,7 +225,10 @@ int oracle_rows(int64_t R, int64_t V, int D, int dtype, const void *H, const voi
             }
             mark_row(row_offsets, item_ids, r, ymap, 0);
             row_loss[i] = lsum;
-            if (dH) for (int d = 0; d < D; ++d) dH[(size_t)i * D + d] = g * s * acc[d];
+            if (dH) {
+                const double w = row_w(row_mask, row_weight, r);
+                for (int d = 0; d < D; ++d) dH[(size_t)i * D + d] = g * s * w * acc[d];
+            }
         }
         free(ymap);
         free(acc);
@@ -208,16 +236,16 @@ int oracle_rows(int64_t R, int64_t V, int D, int dtype, const void *H, const voi
     return err;
 }
 
-/* Item side: dE[i][:] = g*s*sum_{valid r} (sigma(z_r,v) - y_r,v) H[r] for each requested item (all V when
- * items == NULL). */
+/* Item side: dE[i][:] = g*s*sum_{valid r} w_r (sigma(z_r,v) - y_r,v) H[r] for each requested item (all V
+ * when items == NULL). */
 int oracle_items(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
-                 const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
-                 int64_t n_items, const int64_t *items, double *dE) {
+                 const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                 const double *row_weight, double g, int64_t n_items, const int64_t *items, double *dE) {
     int64_t rv;
     int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
     if (st) return st;
     if (!items) n_items = V;
-    double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
+    const double s = norm_scale(R, V, row_mask, row_weight);
     int32_t *sorted = sorted_copy(R, row_offsets, item_ids);
     if (!sorted) return OR_NOMEM;
     int err = 0;
@@ -242,7 +270,11 @@ int oracle_items(int64_t R, int64_t V, int D, int dtype, const void *H, const vo
                 if (!row_mask[r]) continue;
                 double z = dot_rv(H, E, dtype, r, v, D);
                 double y = row_has(row_offsets, sorted, r, (int32_t)v) ? 1.0 : 0.0;
-                double gz = sigmoid(z) - y;
+#if ORACLE_PLANT == 7
+                double gz = sigmoid(z) - y; /* planted: the row weight left out of dE */
+#else
+                double gz = row_w(row_mask, row_weight, r) * (sigmoid(z) - y);
+#endif
 #if ORACLE_PLANT == 4
                 /* planted: transposed operand -- uses E[v] where H[r] belongs */
                 for (int d = 0; d < D; ++d) acc[d] += gz * load_elem(E, dtype, (size_t)v * D + d);
@@ -258,25 +290,23 @@ int oracle_items(int64_t R, int64_t V, int D, int dtype, const void *H, const vo
     return err;
 }
 
-/* Whole problem: loss = s * sum of valid row losses in ascending row order, plus optional row_loss [R],
- * dH [R][D] and dE [V][D]. */
+/* Whole problem: loss = s * sum of weighted valid row losses in ascending row order, plus optional
+ * row_loss [R], dH [R][D] and dE [V][D]. */
 int oracle_full(int64_t R, int64_t V, int D, int dtype, const void *H, const void *E,
-                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask, double g,
-                double *loss, double *row_loss, double *dH, double *dE) {
+                const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                const double *row_weight, double g, double *loss, double *row_loss, double *dH, double *dE) {
     int64_t rv;
     int st = check_inputs(R, V, D, row_offsets, item_ids, row_mask, &rv);
     if (st) return st;
     double *rl = row_loss ? row_loss : (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
     if (!rl) return OR_NOMEM;
-    st = oracle_rows(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, g, R, NULL, rl, dH);
-    if (!st && dE) st = oracle_items(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, g, V, NULL, dE);
+    st = oracle_rows(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, row_weight, g, R, NULL, rl, dH);
+    if (!st && dE)
+        st = oracle_items(R, V, D, dtype, H, E, row_offsets, item_ids, row_mask, row_weight, g, V, NULL, dE);
     if (!st) {
-        double s = rv > 0 ? 1.0 / ((double)rv * (double)V) : 0.0;
-#if ORACLE_PLANT == 2
-        s = 1.0 / ((double)R * (double)V);
-#endif
+        const double s = norm_scale(R, V, row_mask, row_weight);
         double tot = 0.0;
-        for (int64_t r = 0; r < R; ++r) tot += rl[r];
+        for (int64_t r = 0; r < R; ++r) tot += row_w(row_mask, row_weight, r) * rl[r];
         *loss = s * tot;
     }
     if (!row_loss) free(rl);
