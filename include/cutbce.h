@@ -5,12 +5,15 @@
  *   rows r < R carry hidden states H[r] (D values), items v < V carry embeddings E[v]; the logit is
  *   z_rv = H[r] . E[v] (Section III-A). Row r's positive items are a list of ids; y_rv = 1 iff v is in the
  *   list (a repeated id counts once). Rows with row_mask[r] == 0 are padding and take no part.
- *   With R_v = number of valid rows and s = 1 / (R_v * V):
- *     loss   = s * sum_{valid r} sum_v [ max(z,0) + log(1 + exp(-|z|)) - y*z ]      (Eq. (2)-(3) and the
+ *   Valid rows may carry weights w_r (row_weight; w_r = 1 when it is NULL). With W = sum of w_r over the
+ *   valid rows (R_v, the number of valid rows, without weights) and s = 1 / (W * V):
+ *     loss   = s * sum_{valid r} w_r sum_v [ max(z,0) + log(1 + exp(-|z|)) - y*z ]  (Eq. (2)-(3) and the
  *                                                                                   averaging after Eq. (4))
- *     dH[r]  = g * s * sum_v (sigma(z_rv) - y_rv) * E[v]        for valid r, 0 for masked r   (Eq. (4))
- *     dE[v]  = g * s * sum_{valid r} (sigma(z_rv) - y_rv) * H[r]                             (Eq. (4))
- *   where g is the cotangent of the scalar loss. R_v = 0 gives loss 0 and zero gradients.
+ *     dH[r]  = g * s * w_r * sum_v (sigma(z_rv) - y_rv) * E[v]    for valid r, 0 for masked r   (Eq. (4))
+ *     dE[v]  = g * s * sum_{valid r} w_r (sigma(z_rv) - y_rv) * H[r]                          (Eq. (4))
+ *   where g is the cotangent of the scalar loss. W = 0 gives loss 0 and zero gradients. The weights are the
+ *   per-position `weights` of the paper's API call (Listing 1), which the pages do not define: here they turn
+ *   the average over positions into a weighted average; 0/1 weights are the padding mask itself.
  *   The logits Z and their gradient are never written to memory (Section III-B, Table I): every kernel forms
  *   its [rows x items] tile in registers and reduces it on chip.
  *
@@ -54,7 +57,7 @@ typedef enum {
     CUTBCE_ERR_NULL = 1,        /* a required pointer is NULL */
     CUTBCE_ERR_SHAPE = 2,       /* R < 1, V < 1, nnz < 0, or sizes overflow the supported range */
     CUTBCE_ERR_DTYPE = 3,       /* unknown element type */
-    CUTBCE_ERR_ALIGN = 4,       /* H, E, dH, dE, workspace not 16-byte aligned, or int arrays not 4-byte */
+    CUTBCE_ERR_ALIGN = 4,       /* H, E, dH, dE, workspace not 16-byte aligned, or int / float arrays not 4-byte */
     CUTBCE_ERR_WORKSPACE = 5,   /* workspace smaller than cutbce_workspace_size() */
     CUTBCE_ERR_UNSUPPORTED = 6, /* (dtype, D) combination without a kernel: see cutbce_problem */
     CUTBCE_ERR_HIP = 7          /* a HIP launch or runtime call failed */
@@ -80,12 +83,14 @@ typedef struct {
 cutbce_status cutbce_workspace_size(const cutbce_problem *p, size_t *bytes);
 
 /* Forward (Section III-A, Eq. (2)-(3); Section III-C's forward sweep over vocabulary blocks).
+ *   row_weight (device) float [R] or NULL: the weights w_r of the rows (finite, >= 0; read for valid rows
+ *             only). NULL weighs every valid row 1. A valid row of weight 0 adds nothing but is still swept.
  *   loss      (device) float [1]: the scalar loss above.
- *   row_loss  (device) float [R] or NULL: sum_v [softplus(z_rv) - y_rv z_rv] per valid row (not divided by
- *             R_v*V), 0 for masked rows.
+ *   row_loss  (device) float [R] or NULL: sum_v [softplus(z_rv) - y_rv z_rv] per valid row (neither weighted
+ *             nor divided by W*V), 0 for masked rows.
  *   dh_saved  (device) float [R][D] or NULL: when given, the same sweep also forms
- *             s * sum_v (sigma(z_rv) - y_rv) E[v] (the dH of Eq. (4) for g = 1; 0 for masked rows) so that
- *             cutbce_backward can return dH without recomputing the logits for it.
+ *             s * w_r * sum_v (sigma(z_rv) - y_rv) E[v] (the dH of Eq. (4) for g = 1; 0 for masked rows) so
+ *             that cutbce_backward can return dH without recomputing the logits for it.
  *   metrics   (device) int32 [R][4] or NULL: Cut Metrics (Section III-D), counted in the same sweep from the
  *             same float32 logits: TP, FP, FN, TN over the V items of each valid row, an item being predicted
  *             positive iff z_rv > 0 (the section names no threshold: sigma(z) > 1/2 is used); all four are 0
@@ -93,10 +98,11 @@ cutbce_status cutbce_workspace_size(const cutbce_problem *p, size_t *bytes);
  */
 cutbce_status cutbce_forward(const cutbce_problem *p, const void *H, const void *E,
                              const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
-                             float *loss, float *row_loss, float *dh_saved, int32_t *metrics,
-                             void *workspace, size_t workspace_bytes, void *stream);
+                             const float *row_weight, float *loss, float *row_loss, float *dh_saved,
+                             int32_t *metrics, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward (Section III-B, Eq. (4); the custom VJP recomputes logit tiles on chip).
+ *   row_weight (device) float [R] or NULL: as for cutbce_forward (the same weights as the forward call).
  *   grad_loss (device) float [1]: the cotangent g.
  *   dh_saved  (device) float [R][D] or NULL: the forward's dh_saved for these same inputs. When NULL and dH
  *             is requested, dH is computed here by recomputing the logits.
@@ -105,8 +111,8 @@ cutbce_status cutbce_forward(const cutbce_problem *p, const void *H, const void 
  */
 cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void *E,
                               const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
-                              const float *grad_loss, const float *dh_saved, void *dH, void *dE,
-                              void *workspace, size_t workspace_bytes, void *stream);
+                              const float *row_weight, const float *grad_loss, const float *dh_saved, void *dH,
+                              void *dE, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device-side check of the targets: writes to *bad (device int32) the number of ids outside [0, V) plus
  * the number of rows whose offsets decrease, plus 1 if row_offsets[0] != 0 or row_offsets[R] > nnz (ids are

@@ -47,7 +47,8 @@ def test_workspace_has_no_rows_times_vocab_term(name):
     assert ws < 0.5 * W.dense_logits_bytes(cfg.R, cfg.V) or cfg.R * cfg.V < 1e7
 
 
-def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_bytes=None, metrics=None):
+def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_bytes=None, metrics=None,
+                  weight=None):
     lib = B.lib()
     if ws_bytes is None:
         try:
@@ -55,7 +56,8 @@ def _call_forward(p, H=16, E=16, ro=16, ids=16, mask=16, loss=16, ws=256, ws_byt
         except B.CutBCEError:
             ws_bytes = 1 << 40
     vp = ctypes.c_void_p
-    return lib.cutbce_forward(ctypes.byref(p), vp(H), vp(E), vp(ro), vp(ids), vp(mask), vp(loss), None, None,
+    return lib.cutbce_forward(ctypes.byref(p), vp(H), vp(E), vp(ro), vp(ids), vp(mask),
+                              vp(weight) if weight else None, vp(loss), None, None,
                               vp(metrics) if metrics else None, vp(ws), ws_bytes, None)
 
 
@@ -81,6 +83,8 @@ def test_forward_rejects_bad_arguments():
     assert _call_forward(neg_nnz, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE) == 2
     assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE,
                          metrics=FAKE + 2) == 4  # misaligned metrics
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE,
+                         weight=FAKE + 2) == 4  # misaligned row weights
     # nnz > 0 needs item_ids
     assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=0, mask=FAKE, loss=FAKE, ws=FAKE) == 1
 
@@ -92,13 +96,16 @@ def test_backward_and_validate_reject_bad_arguments():
     ws = B.workspace_size(p)
     # grad_loss NULL
     assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None,
-                               vp(FAKE), vp(FAKE), vp(FAKE), ws, None) == 1
+                               None, vp(FAKE), vp(FAKE), vp(FAKE), ws, None) == 1
     # misaligned dE
-    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
-                               vp(FAKE), vp(FAKE + 4), vp(FAKE), ws, None) == 4
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE),
+                               None, vp(FAKE), vp(FAKE + 4), vp(FAKE), ws, None) == 4
+    # misaligned row weights
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE + 2),
+                               vp(FAKE), None, vp(FAKE), vp(FAKE), vp(FAKE), ws, None) == 4
     # workspace too small
-    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
-                               vp(FAKE), vp(FAKE), vp(FAKE), ws - 1, None) == 5
+    assert lib.cutbce_backward(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE),
+                               None, vp(FAKE), vp(FAKE), vp(FAKE), ws - 1, None) == 5
     assert lib.cutbce_validate_targets(ctypes.byref(p), None, vp(FAKE), vp(FAKE), None) == 1
     assert lib.cutbce_validate_targets(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE + 2), None) == 4
     n = ctypes.c_size_t(0)

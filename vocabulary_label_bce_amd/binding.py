@@ -47,8 +47,8 @@ def lib():
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         P = ctypes.POINTER(Problem)
         L.cutbce_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
-        L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
         L.cutbce_targets_to_csr.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp]
         L.cutbce_topk.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
@@ -103,18 +103,20 @@ def alloc_workspace(p: Problem, device) -> torch.Tensor:
 
 
 def forward(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row_loss, dh_saved, ws, stream=None,
-            metrics=None):
-    """cutbce_forward on device tensors (outputs written in place; metrics: int32 [R, 4] or None)."""
+            metrics=None, row_weight=None):
+    """cutbce_forward on device tensors (outputs written in place; metrics: int32 [R, 4] or None;
+    row_weight: float32 [R] or None)."""
     _check(lib().cutbce_forward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
-                                _ptr(row_mask), _ptr(loss), _ptr(row_loss), _ptr(dh_saved), _ptr(metrics),
-                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+                                _ptr(row_mask), _ptr(row_weight), _ptr(loss), _ptr(row_loss), _ptr(dh_saved),
+                                _ptr(metrics), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_saved, dH, dE, ws, stream=None):
+def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_saved, dH, dE, ws, stream=None,
+             row_weight=None):
     """cutbce_backward on device tensors (dH / dE overwritten in place; either may be None)."""
     _check(lib().cutbce_backward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
-                                 _ptr(row_mask), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH), _ptr(dE), _ptr(ws),
-                                 ws.numel() if ws is not None else 0, _stream(stream)))
+                                 _ptr(row_mask), _ptr(row_weight), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH),
+                                 _ptr(dE), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def topk(p: Problem, H, E, row_offsets, item_ids, row_mask, k: int, top_vals, top_ids, hits, ws, stream=None):

@@ -64,6 +64,7 @@ Layout make_layout(const cutbce_problem* p) {
   L.off_row_of = take(sizeof(int32_t) * L.R_pad);
   L.off_compact_of = take(sizeof(int32_t) * L.R);
   L.off_rptr = take(sizeof(int32_t) * 2 * L.R_pad);
+  L.off_wc = take(sizeof(float) * L.R_pad);
   L.off_Hc = take((size_t)L.R_pad * L.D * L.esz);
   L.off_Hrp = take((size_t)L.R_pad * L.D * L.esz);
   L.off_sumH = take(sizeof(double) * L.D);
@@ -186,19 +187,20 @@ cutbce_status cutbce_workspace_size(const cutbce_problem* p, size_t* bytes) {
 }
 
 cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
-                             const int32_t* item_ids, const uint8_t* row_mask, float* loss, float* row_loss,
-                             float* dh_saved, int32_t* metrics, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             const int32_t* item_ids, const uint8_t* row_mask, const float* row_weight,
+                             float* loss, float* row_loss, float* dh_saved, int32_t* metrics, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   Layout L;
   cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
   if (s != CUTBCE_OK) return s;
   if (!loss) return CUTBCE_ERR_NULL;
-  if (misaligned(dh_saved, 16) || misaligned(loss, 4) || misaligned(row_loss, 4) || misaligned(metrics, 4))
+  if (misaligned(dh_saved, 16) || misaligned(loss, 4) || misaligned(row_loss, 4) || misaligned(metrics, 4) ||
+      misaligned(row_weight, 4))
     return CUTBCE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const bool with_dh = dh_saved != nullptr;
-  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_compact(L, ws, row_mask, row_weight, row_offsets, st));
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_prep_e(L, ws, E, with_dh, st));
   TRY(launch_buckets(L, ws, item_ids, true, st));
@@ -208,19 +210,20 @@ cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void*
 }
 
 cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
-                              const int32_t* item_ids, const uint8_t* row_mask, const float* grad_loss,
-                              const float* dh_saved, void* dH, void* dE, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              const int32_t* item_ids, const uint8_t* row_mask, const float* row_weight,
+                              const float* grad_loss, const float* dh_saved, void* dH, void* dE, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   Layout L;
   cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
   if (s != CUTBCE_OK) return s;
   if (!grad_loss) return CUTBCE_ERR_NULL;
-  if (misaligned(dh_saved, 16) || misaligned(dH, 16) || misaligned(dE, 16) || misaligned(grad_loss, 4))
+  if (misaligned(dh_saved, 16) || misaligned(dH, 16) || misaligned(dE, 16) || misaligned(grad_loss, 4) ||
+      misaligned(row_weight, 4))
     return CUTBCE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (!dH && !dE) return CUTBCE_OK;
-  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_compact(L, ws, row_mask, row_weight, row_offsets, st));
   TRY(launch_prep_h(L, ws, H, dE != nullptr, st));
   if (dE) {
     TRY(launch_buckets(L, ws, item_ids, false, st));
@@ -262,7 +265,7 @@ cutbce_status cutbce_topk(const cutbce_problem* p, const void* H, const void* E,
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int kt = kTopKMax;
-  TRY(launch_compact(L, ws, row_mask, row_offsets, st));
+  TRY(launch_compact(L, ws, row_mask, nullptr, row_offsets, st));
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_fill_i32((int32_t*)(ws + L.off_bptr_r), L.nb_r + 1, 0, st));  // no positive buckets
   {

@@ -69,7 +69,7 @@ struct Ctl {           // device control block
   int32_t splits;      // vocabulary splits chosen by the forward sweep
   int32_t bad_ids;     // ids skipped by the bucketing kernels (out of range)
   int32_t pad0;
-  double scale;        // s = 1 / (R_v * V), 0 when R_v == 0
+  double scale;        // s = 1 / (W * V), W = summed weight of the valid rows (R_v without weights); 0 when W == 0
 };
 
 struct Layout {
@@ -82,7 +82,7 @@ struct Layout {
   int rows_per_wg, items_per_wg;
   int64_t n_eblk;     // blocks of the E preparation kernel
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
-  size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_Hc, off_Hrp, off_sumH, off_sumH_part;
+  size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
   size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan;
   size_t scan_elems;
@@ -101,8 +101,8 @@ __host__ __device__ constexpr inline int sweep_waves(int dtype, int D) {
 // ---------------------------------------------------------------------------------------------------------
 // Launchers (each returns the hipError_t of its launches).
 // ---------------------------------------------------------------------------------------------------------
-hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const int32_t* row_offsets,
-                          hipStream_t st);
+hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const float* weight,
+                          const int32_t* row_offsets, hipStream_t st);
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st);
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st);
 hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st);

@@ -6,7 +6,9 @@
 // sum_v z_rv = H[r] . (sum_v E[v]) (a rank-1 identity, evaluated in float64), the unnormalised row loss of
 // "Cut Binary Cross Entropy" Eq. (2)-(3) is
 //   V ln 2 + H[r].sum_v E[v] + sum_splits e - sum_splits p,
-// and dH[r] = s * (sum_splits dH_part + (1/2) sum_v E[v]) (Eq. (4) with sigma split as (sigma - 1/2) + 1/2).
+// and dH[r] = s * w_r * (sum_splits dH_part + (1/2) sum_v E[v]) (Eq. (4) with sigma split as
+// (sigma - 1/2) + 1/2). The loss is s * sum_r w_r * (row loss), rows added in compacted order in float64; w_r
+// is the row's weight (1 without weights) and s = 1 / (W V).
 // With Cut Metrics (Section III-D) the sweep also leaves, per split, the counts of logits predicted positive
 // (z > 0), of positives predicted positive and of positives; TP, FP, FN and TN follow by subtraction.
 #include "common.h"
@@ -30,6 +32,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl, const T* __restrict__ H,
                                                      const uint8_t* __restrict__ mask,
                                                      const int32_t* __restrict__ compact_of,
+                                                     const float* __restrict__ wc,
                                                      const float* __restrict__ dhpart,
                                                      const float2* __restrict__ rowpart,
                                                      const int4* __restrict__ metpart,
@@ -51,12 +54,13 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
   const int S = ctl->splits;
   const int Tt = (ctl->n_valid + RW - 1) / RW;
   const int t = k / RW, loc = k % RW;
-  const double scale = ctl->scale;
+  const double w = (double)wc[k];
+  const double sw = ctl->scale * w;  // s w_r (= s exactly for unit weights)
   if (dh_out) {
     for (int d = lane; d < D; d += 64) {
       double acc = 0.0;
       for (int s = 0; s < S; ++s) acc += (double)dhpart[((int64_t)(s * Tt + t) * RW + loc) * D + d];
-      dh_out[r * D + d] = (float)(scale * (acc + 0.5 * sumE[d]));
+      dh_out[r * D + d] = (float)(sw * (acc + 0.5 * sumE[d]));
     }
   }
   double e = 0.0, p = 0.0;
@@ -88,7 +92,7 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
   const double rl = (double)V * 0.69314718055994530942 + zs + e - p;
   if (lane == 0) {
     if (row_loss) row_loss[r] = (float)rl;
-    rowloss_c[k] = rl;
+    rowloss_c[k] = w * rl;
   }
 }
 
@@ -114,13 +118,15 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
   const Ctl* ctl = (const Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {
     hipLaunchKernelGGL(k_rows_finish<__bf16>, dim3(blocks), dim3(256), 0, st, ctl, (const __bf16*)H, mask,
-                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
+                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_wc),
+                       (const float*)(ws + L.off_dhpart),
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
                        (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);
   } else {
     hipLaunchKernelGGL(k_rows_finish<float>, dim3(blocks), dim3(256), 0, st, ctl, (const float*)H, mask,
-                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_dhpart),
+                       (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_wc),
+                       (const float*)(ws + L.off_dhpart),
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
                        (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);

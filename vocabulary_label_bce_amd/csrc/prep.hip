@@ -59,15 +59,19 @@ __device__ inline int block_excl_scan(int v, int* sh, int& total) {
 
 // ---------------------------------------------------------------------------------------------------------
 // Row compaction: one workgroup walks the mask in chunks of 4096 rows (4 consecutive rows per thread), keeping
-// ascending order.
+// ascending order. Each valid row's weight (1 without weights) goes to wc[k]; their sum W, in float64 (each
+// thread adds its rows in order, then the 1024 partial sums are added in a fixed tree), gives s = 1 / (W V).
 // ---------------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask,
+                                                  const float* __restrict__ weight,
                                                   const int32_t* __restrict__ row_offsets, int64_t R,
                                                   int64_t R_pad, int64_t V, int64_t nnz, Ctl* ctl,
-                                                  int32_t* row_of, int32_t* compact_of, int2* rptr) {
+                                                  int32_t* row_of, int32_t* compact_of, int2* rptr, float* wc) {
   __shared__ int sh[16];
+  __shared__ double shw[16];
   const int tid = threadIdx.x;
   int base = 0;
+  double wsum = 0.0;
   for (int64_t c0 = 0; c0 < R; c0 += 4096) {
     const int64_t r0 = c0 + 4 * tid;
     bool f[4];
@@ -84,6 +88,9 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
       const int64_t r = r0 + j;
       if (r < R) {
         if (f[j]) {
+          const float w = weight ? weight[r] : 1.f;
+          wsum += (double)w;
+          wc[k] = w;
           row_of[k] = (int32_t)r;
           compact_of[r] = k;
           // the row's id range, clamped into [0, nnz] (inconsistent offsets give an empty or shortened range)
@@ -102,20 +109,27 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
   for (int64_t k = nv + tid; k < R_pad; k += 1024) {
     row_of[k] = -1;
     rptr[k] = make_int2(0, 0);
+    wc[k] = 0.f;
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+  if (lane_id() == 0) shw[tid / 64] = wsum;
+  __syncthreads();
   if (tid == 0) {
+    double W = 0.0;
+    for (int i = 0; i < 16; ++i) W += shw[i];
     ctl->n_valid = nv;
     ctl->splits = 0;
     ctl->bad_ids = 0;
-    ctl->scale = nv > 0 ? 1.0 / ((double)nv * (double)V) : 0.0;
+    ctl->scale = W != 0.0 ? 1.0 / (W * (double)V) : 0.0;
   }
 }
 
-hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const int32_t* row_offsets,
-                          hipStream_t st) {
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, row_offsets, L.R, L.R_pad, L.V, L.nnz,
+hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const float* weight,
+                          const int32_t* row_offsets, hipStream_t st) {
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, weight, row_offsets, L.R, L.R_pad, L.V, L.nnz,
                      (Ctl*)(ws + L.off_ctl), (int32_t*)(ws + L.off_row_of), (int32_t*)(ws + L.off_compact_of),
-                     (int2*)(ws + L.off_rptr));
+                     (int2*)(ws + L.off_rptr), (float*)(ws + L.off_wc));
   return hipGetLastError();
 }
 
@@ -132,18 +146,42 @@ __device__ inline void set_run<float>(float& run, const float* tile, int D, int 
   run = tile[acc_pos(g, lane / 32) * D + db * 32 + lane % 32];
 }
 
+// The same run with each value times its row's weight w[row] (a weight of 1 leaves it unchanged; others round
+// once to the element type).
+template <typename T>
+__device__ inline void set_run_w(typename Elem<T>::Op& run, const T* tile, const float* w, int D, int db, int g,
+                                 int lane);
+template <>
+__device__ inline void set_run_w<__bf16>(bf16x8& run, const __bf16* tile, const float* w, int D, int db, int g,
+                                         int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = acc_pos(g * 8 + j, lane / 32);
+    run[j] = (__bf16)((float)tile[row * D + db * 32 + lane % 32] * w[row]);
+  }
+}
+template <>
+__device__ inline void set_run_w<float>(float& run, const float* tile, const float* w, int D, int db, int g,
+                                        int lane) {
+  const int row = acc_pos(g, lane / 32);
+  run = tile[row * D + db * 32 + lane % 32] * w[row];
+}
+
 // ---------------------------------------------------------------------------------------------------------
-// H preparation: block = 32 compacted rows. Hc[k] = H[row_of[k]] (0 for padding), Hrp = slot-packed Hc
-// blocks, per-block column sums (float64) of the valid rows.
+// H preparation: block = 32 compacted rows. Hc[k] = H[row_of[k]] (0 for padding), Hrp = slot-packed blocks of
+// the weighted rows wc[k] Hc[k] (the B operand of the dE sweep's gradient GEMM, so each row's contribution to
+// dE carries its weight), per-block float64 column sums of the weighted rows (the dE sweep's 1/2 sum_r w_r H[r]).
 // ---------------------------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const int32_t* __restrict__ row_of,
-                                                int D, T* __restrict__ Hc, T* __restrict__ Hrp,
-                                                double* __restrict__ sum_part) {
+                                                const float* __restrict__ wc, int D, T* __restrict__ Hc,
+                                                T* __restrict__ Hrp, double* __restrict__ sum_part) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
+  __shared__ float wt[32];
   const int tid = threadIdx.x;
   const int64_t k0 = (int64_t)blockIdx.x * 32;
+  if (tid < 32) wt[tid] = wc[k0 + tid];
   // gather rows (16-byte units)
   const int upr = D * (int)sizeof(T) / 16;  // 16-byte units per row
   for (int u = tid; u < 32 * upr; u += 256) {
@@ -162,13 +200,13 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
       const int lane = q % 64, g = (q / 64) % Elem<T>::kGroups, db = q / (64 * Elem<T>::kGroups);
       const int64_t o = slot_off<T>(D, db, g, lane);
       typename Elem<T>::Op run;
-      set_run<T>(run, tile, D, db, g, lane);
+      set_run_w<T>(run, tile, wt, D, db, g, lane);
       *(typename Elem<T>::Op*)(dst + o) = run;
     }
   }
   for (int d = tid; d < D; d += 256) {
     double s = 0.0;
-    for (int rr = 0; rr < 32; ++rr) s += (double)(float)tile[rr * D + d];
+    for (int rr = 0; rr < 32; ++rr) s += (double)(float)tile[rr * D + d] * (double)wt[rr];
     sum_part[blockIdx.x * (int64_t)D + d] = s;
   }
 }
@@ -207,11 +245,13 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   const size_t sm = (size_t)32 * L.D * L.esz;
   if (L.dtype == 1) {
     hipLaunchKernelGGL(k_prep_h<__bf16>, dim3((unsigned)nblk), dim3(256), sm, st, (const __bf16*)H,
-                       (const int32_t*)(ws + L.off_row_of), L.D, (__bf16*)(ws + L.off_Hc),
+                       (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
+                       (__bf16*)(ws + L.off_Hc),
                        want_hrp ? (__bf16*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
   } else {
     hipLaunchKernelGGL(k_prep_h<float>, dim3((unsigned)nblk), dim3(256), sm, st, (const float*)H,
-                       (const int32_t*)(ws + L.off_row_of), L.D, (float*)(ws + L.off_Hc),
+                       (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
+                       (float*)(ws + L.off_Hc),
                        want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
   }
   hipError_t e = hipGetLastError();

@@ -11,6 +11,16 @@ import torch
 from . import binding as B
 
 
+def _weights(row_weight, H):
+    """float32 [R] row weights on H's device, or None."""
+    if row_weight is None:
+        return None
+    w = row_weight.to(device=H.device, dtype=torch.float32).reshape(-1).contiguous()
+    if w.numel() != H.shape[0]:
+        raise ValueError("row_weight must have R entries")
+    return w
+
+
 def _prep(H, E, row_offsets, item_ids, row_mask):
     if not (H.is_cuda and E.is_cuda):
         raise ValueError("cut_bce runs on the GPU only: H and E must be device tensors")
@@ -31,40 +41,42 @@ def _prep(H, E, row_offsets, item_ids, row_mask):
 
 class _CutBCE(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, E, row_offsets, item_ids, row_mask):
+    def forward(ctx, H, E, row_offsets, item_ids, row_mask, row_weight):
         p = B.problem_of(H, E, item_ids)
         ws = B.alloc_workspace(p, H.device)
         loss = torch.empty(1, dtype=torch.float32, device=H.device)
         dh_saved = None
         if ctx.needs_input_grad[0]:
             dh_saved = torch.empty(H.shape, dtype=torch.float32, device=H.device)
-        B.forward(p, H, E, row_offsets, item_ids, row_mask, loss, None, dh_saved, ws)
-        ctx.save_for_backward(H, E, row_offsets, item_ids, row_mask, dh_saved)
+        B.forward(p, H, E, row_offsets, item_ids, row_mask, loss, None, dh_saved, ws, row_weight=row_weight)
+        ctx.save_for_backward(H, E, row_offsets, item_ids, row_mask, dh_saved, row_weight)
         ctx.p = p
         return loss[0]
 
     @staticmethod
     def backward(ctx, g):
-        H, E, row_offsets, item_ids, row_mask, dh_saved = ctx.saved_tensors
+        H, E, row_offsets, item_ids, row_mask, dh_saved, row_weight = ctx.saved_tensors
         p = ctx.p
         g = g.reshape(1).to(dtype=torch.float32).contiguous()
         dH = torch.empty_like(H) if ctx.needs_input_grad[0] else None
         dE = torch.empty_like(E) if ctx.needs_input_grad[1] else None
         if dH is not None or dE is not None:
             ws = B.alloc_workspace(p, H.device)
-            B.backward(p, H, E, row_offsets, item_ids, row_mask, g, dh_saved, dH, dE, ws)
-        return dH, dE, None, None, None
+            B.backward(p, H, E, row_offsets, item_ids, row_mask, g, dh_saved, dH, dE, ws, row_weight=row_weight)
+        return dH, dE, None, None, None, None
 
 
-def cut_bce(H, E, row_offsets, item_ids, row_mask):
+def cut_bce(H, E, row_offsets, item_ids, row_mask, row_weight=None):
     """Exact full-vocabulary BCE loss over logits H @ E^T, averaged over valid rows and all V items.
 
     H [R, D] and E [V, D] (float32 or bfloat16, on the GPU); positives of row r are
     item_ids[row_offsets[r]:row_offsets[r+1]] (any order, repeats count once); row_mask [R] marks valid rows.
-    Returns a 0-d float32 tensor; gradients flow to H and E.
+    row_weight [R] (optional, finite and >= 0): per-row weights; the loss becomes the weighted average
+    sum_r w_r sum_v L / (W V) over valid rows, W = sum of their weights (no weights: W = number of valid rows).
+    Returns a 0-d float32 tensor; gradients flow to H and E (not to the weights).
     """
     H, E, row_offsets, item_ids, row_mask = _prep(H, E, row_offsets, item_ids, row_mask)
-    return _CutBCE.apply(H, E, row_offsets, item_ids, row_mask)
+    return _CutBCE.apply(H, E, row_offsets, item_ids, row_mask, _weights(row_weight, H))
 
 
 def dense_to_csr(targets, pad_id: int = -1):
@@ -86,10 +98,11 @@ def dense_to_csr(targets, pad_id: int = -1):
 
 def cut_binary_cross_entropy(activations, embeddings, targets, weights=None, pad_id: int = -1):
     """The paper's Listing 1 call shape: activations [B, N, D], embeddings [V, D], targets [B, N, L] (ids, slots
-    equal to `pad_id` are padding), weights [B, N] per position or None (all positions train).
+    equal to `pad_id` are padding), weights [B, N] per position or None (all positions weigh 1).
 
-    The weights are read as a 0/1 mask: a position with weight 0 is padding and is left out of the average,
-    every other position is trained. Weights other than 0 and 1 raise (checking them reads the tensor back).
+    A position of weight 0 is padding: it is left out, and so are its targets. The others are averaged with
+    their weights: loss = sum_pos w sum_v L / (sum_pos w * V). 0/1 weights give the plain average over the
+    trained positions. Weights must be finite and >= 0 (not checked: that would read them back to the host).
     Returns the scalar loss; gradients flow to activations and embeddings.
     """
     B_, N = activations.shape[0], activations.shape[1]
@@ -97,12 +110,10 @@ def cut_binary_cross_entropy(activations, embeddings, targets, weights=None, pad
     row_offsets, item_ids = dense_to_csr(targets, pad_id)
     if weights is None:
         mask = torch.ones(B_ * N, dtype=torch.uint8, device=H.device)
-    else:
-        w = weights.reshape(B_ * N)
-        if w.dtype.is_floating_point and not bool(((w == 0) | (w == 1)).all()):
-            raise ValueError("weights other than 0 and 1 are not supported: a weight marks a position as trained")
-        mask = (w != 0).to(torch.uint8)
-    return cut_bce(H, embeddings, row_offsets, item_ids, mask)
+        return cut_bce(H, embeddings, row_offsets, item_ids, mask)
+    w = weights.reshape(B_ * N).to(device=H.device)
+    mask = (w != 0).to(torch.uint8)
+    return cut_bce(H, embeddings, row_offsets, item_ids, mask, row_weight=w)
 
 
 def topk(H, E, k: int = 8, row_offsets=None, item_ids=None, row_mask=None, ws=None):
@@ -146,14 +157,15 @@ class Workspace:
         self.dH = torch.empty_like(H)
         self.dE = torch.empty_like(E)
 
-    def forward(self, H, E, row_offsets, item_ids, row_mask, stream=None):
+    def forward(self, H, E, row_offsets, item_ids, row_mask, stream=None, row_weight=None):
         B.forward(self.p, H, E, row_offsets, item_ids, row_mask, self.loss, self.row_loss, self.dh_saved, self.ws,
-                  stream, metrics=self.metrics)
+                  stream, metrics=self.metrics, row_weight=row_weight)
         return self.loss
 
     def backward(self, H, E, row_offsets, item_ids, row_mask, grad=None, want_dH=True, want_dE=True,
-                 use_saved=True, stream=None):
+                 use_saved=True, stream=None, row_weight=None):
         g = self.grad if grad is None else grad
         B.backward(self.p, H, E, row_offsets, item_ids, row_mask, g, self.dh_saved if use_saved else None,
-                   self.dH if want_dH else None, self.dE if want_dE else None, self.ws, stream)
+                   self.dH if want_dH else None, self.dE if want_dE else None, self.ws, stream,
+                   row_weight=row_weight)
         return (self.dH if want_dH else None), (self.dE if want_dE else None)
