@@ -44,3 +44,36 @@ def test_traffic_scales_by_the_copy_kernel(tmp_path):
     assert d["fetch_kib_per_dispatch"] == [1500.0, 1500.0]
     assert abs(d["fetch_bytes_per_launch"] - 1500.0 * 1024 * 2.0) < 1e-6
     assert abs(d["bytes_per_launch"] - (1500.0 * 1024 * 2.0 + 10.0 * 1024)) < 1e-6
+
+
+def test_counter_report_derives_clock_and_mfma_busy(tmp_path):
+    # two passes over one kernel: pass 1 carries the MFMA counters, pass 2 GRBM_GUI_ACTIVE, each with its own
+    # dispatch duration (1 ms and 2 ms); 1024 SIMDs, 8 XCDs, 2 GHz
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+    def write(path, rows):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=fields)
+            w.writeheader()
+            for r in rows:
+                w.writerow(r)
+
+    a, b = tmp_path / "p1.csv", tmp_path / "p2.csv"
+    busy = 0.5 * 1024 * 2.0 * 1e6  # half of 1024 SIMDs x 2 GHz x 1 ms
+    write(a, [dict(Dispatch_Id=1, Kernel_Name="k_itemsI<x>", Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES",
+                   Counter_Value=busy, Start_Timestamp=0, End_Timestamp=1_000_000),
+              dict(Dispatch_Id=1, Kernel_Name="k_itemsI<x>", Counter_Name="SQ_INSTS_MFMA", Counter_Value=busy / 32,
+                   Start_Timestamp=0, End_Timestamp=1_000_000),
+              dict(Dispatch_Id=1, Kernel_Name="k_itemsI<x>", Counter_Name="SQ_INSTS_VALU",
+                   Counter_Value=9 * busy / 32, Start_Timestamp=0, End_Timestamp=1_000_000),
+              dict(Dispatch_Id=2, Kernel_Name="other", Counter_Name="SQ_INSTS_MFMA", Counter_Value=1.0,
+                   Start_Timestamp=0, End_Timestamp=5)])
+    write(b, [dict(Dispatch_Id=1, Kernel_Name="k_itemsI<x>", Counter_Name="GRBM_GUI_ACTIVE",
+                   Counter_Value=8 * 2.0 * 2e6, Start_Timestamp=0, End_Timestamp=2_000_000)])
+    means, durs = P.counter_means([str(a), str(b)], "k_itemsI")
+    d = P.counter_report(means, durs)
+    clock = [v for k, v in d.items() if k.startswith("shader clock")][0]
+    frac = [v for k, v in d.items() if k.startswith("MFMA pipe busy")][0]
+    assert abs(clock - 2.0) < 1e-12 and abs(frac - 0.5) < 1e-12
+    assert d["MFMA busy cycles per MFMA instruction"] == 32.0
+    assert abs(d["VALU instructions per MFMA (SQ_INSTS_VALU counts MFMA too; excluded)"] - 8.0) < 1e-12
