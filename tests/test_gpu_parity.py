@@ -77,6 +77,11 @@ CASES = [
     # unsorted ids with repeats
     ("bf16_unsorted_dups", dict(R=100, V=300, D=64, dtype="bf16", seed=10, h_std=0.5, e_std=0.5,
                                 pos_per_row=(1, 20), mask_frac=0.1, dup_frac=0.5, sort_ids=False)),
+    # rows averaging more than 32 ids: positives bucketed one wave per row, runs reserved by one atomic each
+    ("bf16_dense_positives", dict(R=70, V=3000, D=128, dtype="bf16", seed=11, h_std=0.3, e_std=0.3,
+                                  pos_per_row=(40, 160), mask_frac=0.1, zipf_s=0.8)),
+    ("f32_dense_positives_unsorted", dict(R=45, V=2500, D=64, dtype="f32", seed=12, h_std=0.4, e_std=0.4,
+                                          pos_per_row=(33, 200), mask_frac=0.1, dup_frac=0.3, sort_ids=False)),
 ]
 
 

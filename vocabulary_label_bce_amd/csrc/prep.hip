@@ -385,18 +385,23 @@ static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, hipStream_
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Positive-id buckets. One wave per compacted row; pairs (compact row k, item v) go to
+// Positive-id buckets. Pairs (compact row k, item v) go to
 //   rows side : bucket (k / rows_per_wg) * n_vs + v / 32      (forward sweep: row tile x item step)
 //   items side: bucket (v / items_per_wg) * n_rs + k / 32     (backward sweep: item tile x row step)
 // Ids outside [0, V) are skipped and counted. Order inside a bucket is irrelevant: the sweeps OR the
 // positives into a per-lane bit mask, which also makes a repeated id count once.
+// Two forms, chosen from the mean row length:
+//  - k_bucket: 8 lanes per row, one atomic per id (rows holding a handful of ids);
+//  - k_bucket_runs: one wave per row, 64 ids at a time. Consecutive lanes whose ids fall in the same bucket
+//    (sorted ids of a long row mostly do) form a run; the run's first lane reserves the whole run with one
+//    atomic and the others take the following slots. With many ids per row and hot items, one atomic per id
+//    serialises on the hot buckets' counters.
 // ---------------------------------------------------------------------------------------------------------
 template <bool kScatter>
 __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
                                                 const int32_t* __restrict__ ids, int64_t V, bool rows_side,
                                                 int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
                                                 int2* __restrict__ pairs, int* bad) {
-  // 8 lanes per compact row (rows hold a handful of ids in the usual workloads)
   const int64_t k = (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8;
   const int sub = threadIdx.x % 8;
   if (k >= ctl->n_valid) return;
@@ -419,6 +424,48 @@ __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, con
   if (!kScatter && nbad) atomicAdd(bad, nbad);
 }
 
+template <bool kScatter>
+__global__ void __launch_bounds__(256) k_bucket_runs(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
+                                                     const int32_t* __restrict__ ids, int64_t V, bool rows_side,
+                                                     int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
+                                                     int2* __restrict__ pairs, int* bad) {
+  const int64_t k = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // one row per wave
+  const int lane = lane_id();
+  if (k >= ctl->n_valid) return;  // the whole wave
+  const int2 rp = rptr[k];
+  int nbad = 0;
+  for (int p0 = rp.x; p0 < rp.y; p0 += 64) {  // uniform across the wave
+    const int p = p0 + lane;
+    long long b = -1;  // bucket, or -1 past the row's end and for ids outside [0, V)
+    int v = 0;
+    if (p < rp.y) {
+      v = ids[p];
+      if (v < 0 || v >= V)
+        ++nbad;
+      else
+        b = rows_side ? (k / tile) * nsteps_minor + v / 32 : (v / tile) * nsteps_minor + k / 32;
+    }
+    // a run starts at lane 0 and wherever the bucket differs from the previous lane's
+    const long long prev = __shfl_up(b, 1, 64);
+    const unsigned long long starts = __ballot(lane == 0 || b != prev);
+    const unsigned long long upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // lanes 0..lane
+    const int head = 63 - __clzll(starts & upto);                               // lane 0 is always a start
+    const unsigned long long after = starts & ~upto;
+    const int end = after ? __ffsll((long long)after) - 1 : 64;
+    int base = 0;
+    if (b >= 0 && lane == head) base = atomicAdd(&cnt[b], end - head);
+    if (kScatter) {
+      base = __shfl(base, head, 64);
+      if (b >= 0) pairs[base + (lane - head)] = make_int2((int)k, v);
+    }
+  }
+  if (!kScatter) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) nbad += __shfl_xor(nbad, o, 64);
+    if (lane == 0 && nbad) atomicAdd(bad, nbad);
+  }
+}
+
 hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st) {
   const int64_t nb = rows_side ? L.nb_r : L.nb_i;
   int32_t* bptr = (int32_t*)(ws + (rows_side ? L.off_bptr_r : L.off_bptr_i));
@@ -429,10 +476,12 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   const int64_t minor = rows_side ? L.n_vs : L.n_rs;
   hipError_t e = launch_fill_i32(bptr, nb + 1, 0, st);
   if (e != hipSuccess) return e;
-  const int64_t blocks = L.R_pad / 32;  // 32 rows of 8 lanes per 256-thread block
+  // wave-per-row runs when rows average more than 32 ids (host-side sizes only)
+  const bool runs = L.nnz > 32 * L.R;
+  const int64_t blocks = runs ? L.R_pad / 4 : L.R_pad / 32;  // rows per 256-thread block: 4 or 32
   if (L.nnz > 0) {
-    hipLaunchKernelGGL(k_bucket<false>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
-                       (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bptr,
+    hipLaunchKernelGGL(runs ? k_bucket_runs<false> : k_bucket<false>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bptr,
                        (int2*)nullptr, &ctl->bad_ids);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -442,8 +491,8 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
     if (cblocks > 65536) cblocks = 65536;
     hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cblocks), dim3(256), 0, st, bfill, (const int32_t*)bptr, nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st, ctl,
-                       (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bfill, pairs,
+    hipLaunchKernelGGL(runs ? k_bucket_runs<true> : k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bfill, pairs,
                        (int*)nullptr);
   }
   return hipGetLastError();
