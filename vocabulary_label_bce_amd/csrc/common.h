@@ -65,7 +65,7 @@ __host__ __device__ constexpr inline int64_t slot_off(int D, int db, int g, int 
 // Workspace layout (computed on the host, passed by value to kernels that need pointers into it).
 // ---------------------------------------------------------------------------------------------------------
 struct Ctl {           // device control block
-  int32_t n_valid;     // R_v
+  int32_t n_valid;     // R_v, the number of valid rows
   int32_t splits;      // vocabulary splits chosen by the forward sweep
   int32_t bad_ids;     // ids skipped by the bucketing kernels (out of range)
   int32_t pad0;

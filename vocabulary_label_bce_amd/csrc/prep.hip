@@ -1,8 +1,9 @@
 // Preparation kernels of the CutBCE sweeps (all HBM-bound, small next to the sweeps):
-//   * row compaction: the list of valid rows and R_v from the row mask (padding positions are excluded from
-//     the average, "Cut Binary Cross Entropy" Section III-B after Eq. (4)), with no host synchronisation;
-//   * H preparation: valid rows gathered into a dense, zero-padded Hc, their slot-packed copy Hrp (second
-//     GEMM operand of the dE sweep) and the column sum of the valid rows;
+//   * row compaction: the list of valid rows, their weights and s = 1 / (W V) from the row mask and weights
+//     (padding positions are excluded from the average, "Cut Binary Cross Entropy" Section III-B after
+//     Eq. (4)), with no host synchronisation;
+//   * H preparation: valid rows gathered into a dense, zero-padded Hc, the slot-packed copy Hrp of the
+//     weighted rows (second GEMM operand of the dE sweep) and the weighted column sum of the valid rows;
 //   * E preparation: the slot-packed copy Evp (second GEMM operand of the forward/dH sweep) and sum_v E[v];
 //   * positive-id buckets: the sparse targets (Listing 1 keeps them as ids, never as a multi-hot Y) grouped
 //     by the (tile, step) of each sweep, so a wave finds the positives of its current 32x32 logit tile with
