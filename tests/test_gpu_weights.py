@@ -137,3 +137,57 @@ def test_autograd_and_listing1_weights_match_oracle():
     l2 = cut_bce(H2, E.cuda(), torch.from_numpy(ro).cuda(), torch.from_numpy(ids).cuda(),
                  torch.from_numpy((wf != 0).astype(np.uint8)).cuda(), row_weight=torch.from_numpy(wf).cuda())
     assert abs(l2.item() - ref["loss"]) <= 1e-4 * abs(ref["loss"])
+
+
+def test_cut_metrics_ignore_weights():
+    p = {k: v.cuda() for k, v in W.custom_problem(180, 2000, 64, dtype="bf16", seed=70, h_std=0.5, e_std=0.5,
+                                                    pos_per_row=(1, 8), mask_frac=0.2).items()}
+    out = []
+    for wt in (None, torch.from_numpy(_weights(180, 70)).cuda()):
+        ws = Workspace(p["H"], p["E"], p["item_ids"], want_metrics=True)
+        ws.forward(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], row_weight=wt)
+        torch.cuda.synchronize()
+        out.append(ws.metrics.cpu().clone())
+    assert torch.equal(out[0], out[1])
+
+
+def test_graph_replay_reads_new_weights():
+    """A captured forward + backward reads the weights anew on every replay."""
+    p = W.custom_problem(200, 3000, 128, dtype="bf16", seed=71, h_std=0.3, e_std=0.3, pos_per_row=(1, 6),
+                         mask_frac=0.2)
+    d = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in p.items()}
+    args = (d["H"], d["E"], d["row_offsets"], d["item_ids"], d["row_mask"])
+    w1 = torch.from_numpy(_weights(200, 71)).cuda()
+    w2 = torch.from_numpy(_weights(200, 72)).cuda()
+    wbuf = w1.clone()
+    ws = Workspace(d["H"], d["E"], d["item_ids"])
+    g = torch.tensor([0.5], device="cuda")
+
+    def step():
+        ws.forward(*args, row_weight=wbuf)
+        return ws.backward(*args, grad=g, row_weight=wbuf)
+
+    refs = []
+    for w in (w1, w2):
+        wbuf.copy_(w)
+        dH, dE = step()
+        torch.cuda.synchronize()
+        refs.append((ws.loss.clone(), dH.clone(), dE.clone()))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdH, gdE = step()
+    torch.cuda.synchronize()
+    for k in (0, 1, 0):
+        wbuf.copy_((w1, w2)[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ws.loss, refs[k][0])
+        assert torch.equal(gdH, refs[k][1])
+        assert torch.equal(gdE, refs[k][2])
