@@ -146,3 +146,31 @@ def test_library_source_never_allocates_device_memory():
     for f in os.listdir(csrc):
         txt = open(os.path.join(csrc, f)).read()
         assert "hipMalloc" not in txt and "hipFree(" not in txt, f
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No CPU fallback: with libcutbce.so absent the binding raises before any computation."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libcutbce.so"))
+    with pytest.raises(B.CutBCEError, match="not built"):
+        B.lib()
+    with pytest.raises(B.CutBCEError):
+        B.workspace_size(B.problem(64, 4096, 100, 64, B.BF16))
+
+
+def test_product_modules_never_import_the_oracle():
+    import ast
+    import os
+
+    pkg = os.path.join(os.path.dirname(__file__), "..", "vocabulary_label_bce_amd")
+    for name in os.listdir(pkg):
+        if not name.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(pkg, name)).read())
+        for node in ast.walk(tree):
+            mods = []
+            if isinstance(node, ast.Import):
+                mods = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                mods = [node.module or ""]
+            assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
