@@ -571,16 +571,17 @@ struct Engine {
   __device__ inline void epilogue(int j, int pb, int pe, const f32x16& z, GPack<T>& g, float& e_acc, float& posz,
                                   int* met, TopK<KT ? KT : 1>* tk) {
     if constexpr (KT > 0) {
-      // scoring: keep the lane's best items (real items only; the last step may hold padding). The lane's best
-      // new logit decides whether any insertion is needed; after the first steps it rarely is.
-      // Only the values above the lane's current k-th best are inserted, one at a time, picked by a select
-      // chain (no dynamic register indexing).
-      const int item0 = (j0 + j) * 32 + (lane / 32) * 4;
+      // scoring: keep the lane's best items (real items only; the last step may hold padding). Only the values
+      // above the lane's current k-th best are inserted, one at a time, picked by a select chain (no dynamic
+      // register indexing). Items past the vocabulary exist only in its last step: the lane's bound (32-bit,
+      // V < 2^31) is all-pass elsewhere.
       const float thr = tk->last();
+      const int item0 = (j0 + j) * 32 + (lane / 32) * 4;
+      const int lim = (int64_t)(j0 + j + 1) * 32 > nX ? (int)nX - item0 : 32;  // items of this lane below V
       uint32_t cand = 0u;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        cand |= (z[i] > thr && item0 + (i / 4) * 8 + (i % 4) < nX) ? (1u << i) : 0u;  // item acc_pos(i, lane / 32)
+      for (int i = 0; i < 16; ++i)  // item acc_pos(i, lane / 32)
+        cand |= (z[i] > thr && (i / 4) * 8 + (i % 4) < lim) ? (1u << i) : 0u;
       while (cand) {
         const int i = __builtin_ctz(cand);
         cand &= cand - 1u;
