@@ -151,8 +151,8 @@ cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t *
  * (kind 0: forward rows sweep, kind 1: backward dE sweep, kind 2: the scoring sweep of cutbce_topk) is
  * bracketed by HIP events recorded on the launch stream. cutbce_profile_read waits for those events and
  * returns, per kind, the summed milliseconds and the number of launches since the last enable/read, then
- * clears them. This is the only state the library keeps
- * across calls; it is off by default. Enabling (on != 0) clears previous records; at most 65536 launches are
+ * clears them. Besides the launch data cached per kernel and device (see the conventions above), this is the
+ * only state the library keeps across calls; it is off by default. Enabling (on != 0) clears previous records; at most 65536 launches are
  * recorded (later ones are not timed). Not thread-safe. */
 cutbce_status cutbce_profile_enable(int on);
 cutbce_status cutbce_profile_read(double *ms, int64_t *launches, int n_kinds);
@@ -160,7 +160,8 @@ cutbce_status cutbce_profile_read(double *ms, int64_t *launches, int n_kinds);
 /* Static description of a status code (host). */
 const char *cutbce_status_string(cutbce_status s);
 
-/* Library version as major*10000 + minor*100 + patch (host). */
+/* Library version as major*10000 + minor*100 + patch (host). 0.2.0 added row_weight to cutbce_forward and
+ * cutbce_backward. */
 int cutbce_version(void);
 
 #ifdef __cplusplus

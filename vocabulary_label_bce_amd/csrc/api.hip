@@ -162,7 +162,7 @@ cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E
 
 extern "C" {
 
-int cutbce_version(void) { return 103; }
+int cutbce_version(void) { return 200; }
 
 const char* cutbce_status_string(cutbce_status s) {
   switch (s) {
