@@ -623,6 +623,429 @@ struct Engine {
   }
 };
 
+// ---------------------------------------------------------------------------------------------------------
+// Epilogue of one 32x32 logit tile (16 values per lane) as a fixed list of vector operations, so that the
+// interleaved engine can hand out an equal share of them after each MFMA. The arithmetic is that of epi_rows
+// (forward: w = 1 + e^-z, products over pairs and quads, one reciprocal per quad, log2 of the tile product) and
+// of epi_items (backward: c = 1/(1 + e^-z) - 1/2), in the same association, so both engines give the same bits.
+// CVT packs two c values of the previous step into the bf16 G operand.
+// ---------------------------------------------------------------------------------------------------------
+struct EpiState {
+  float w[16], w2[8], w4[4], r4[4], ra[4], rb[4];
+  float p01, p23, wp, lg, e_inc;
+  bool slow;
+  bf16x8 g[2];
+};
+
+template <bool FWD, bool GRAD, int NSLOT>
+struct EpiOps {
+  enum { kCvt = 0, kT, kE, kW, kM2, kM4, kR, kA, kB, kF, kWp, kLog, kEi, kCmp, kRc, kS };
+  struct Tbl {
+    short op[128];
+    short start[34];
+    int n, npre;
+  };
+  // Natural order: the first G half is packed before any MFMA (pre-slot), the second half right after; then
+  // pairs of logits through exp, the pair and quad products, and each quad's batch inversion one pair later
+  // (so the reciprocal's latency is covered); the tile product and its log come last.
+  static constexpr Tbl make() {
+    Tbl t{};
+    int n = 0;
+    auto push = [&](int kind, int arg) { t.op[n++] = (short)(kind * 64 + arg); };
+    if (GRAD)
+      for (int p = 0; p < 4; ++p) push(kCvt, p);
+    t.npre = n;
+    for (int p = 0; p < 8; ++p) {
+      push(kT, 2 * p);
+      push(kT, 2 * p + 1);
+      if (GRAD && p == 0)
+        for (int q = 4; q < 8; ++q) push(kCvt, q);
+      push(kE, 2 * p);
+      push(kE, 2 * p + 1);
+      push(kW, 2 * p);
+      push(kW, 2 * p + 1);
+      if (FWD) {
+        push(kM2, p);
+        if (p & 1) {
+          push(kM4, p / 2);
+          if (GRAD) push(kR, p / 2);
+        }
+        if (GRAD && p >= 2 && !(p & 1)) {
+          const int q = p / 2 - 1;
+          push(kA, q);
+          push(kB, q);
+          for (int j = 0; j < 4; ++j) push(kF, 4 * q + j);
+        }
+      } else {
+        push(kRc, 2 * p);
+        push(kRc, 2 * p + 1);
+        push(kS, 2 * p);
+        push(kS, 2 * p + 1);
+      }
+    }
+    if (FWD) {
+      if (GRAD) {
+        push(kA, 3);
+        push(kB, 3);
+        for (int j = 0; j < 4; ++j) push(kF, 12 + j);
+      }
+      push(kWp, 0);
+      push(kWp, 1);
+      push(kWp, 2);
+      push(kLog, 0);
+      push(kEi, 0);
+      push(kCmp, 0);
+    }
+    t.n = n;
+    for (int j = 0; j <= NSLOT; ++j) t.start[j] = (short)(t.npre + (n - t.npre) * j / (NSLOT > 0 ? NSLOT : 1));
+    return t;
+  }
+  static constexpr Tbl tbl = make();
+
+  template <int OPC>
+  __device__ static inline void op(const f32x16& z, float* c, EpiState& s) {
+    constexpr int kind = OPC / 64, a = OPC % 64;
+    if constexpr (kind == kCvt) {
+      s.g[a / 4][2 * (a % 4)] = (__bf16)c[2 * a];
+      s.g[a / 4][2 * (a % 4) + 1] = (__bf16)c[2 * a + 1];
+    } else if constexpr (kind == kT) {
+      s.w[a] = z[a] * -kLog2e;
+    } else if constexpr (kind == kE) {
+      s.w[a] = __builtin_amdgcn_exp2f(s.w[a]);
+    } else if constexpr (kind == kW) {
+      s.w[a] = 1.f + s.w[a];
+    } else if constexpr (kind == kM2) {
+      s.w2[a] = s.w[2 * a] * s.w[2 * a + 1];
+    } else if constexpr (kind == kM4) {
+      s.w4[a] = s.w2[2 * a] * s.w2[2 * a + 1];
+    } else if constexpr (kind == kR) {
+      s.r4[a] = __builtin_amdgcn_rcpf(s.w4[a]);
+    } else if constexpr (kind == kA) {
+      s.ra[a] = s.r4[a] * s.w2[2 * a + 1];
+    } else if constexpr (kind == kB) {
+      s.rb[a] = s.r4[a] * s.w2[2 * a];
+    } else if constexpr (kind == kF) {
+      // c[4q] = ra w[4q+1], c[4q+1] = ra w[4q], c[4q+2] = rb w[4q+3], c[4q+3] = rb w[4q+2]  (minus 1/2)
+      c[a] = ((a % 4) < 2 ? s.ra[a / 4] : s.rb[a / 4]) * s.w[a ^ 1] - 0.5f;
+    } else if constexpr (kind == kWp) {
+      if constexpr (a == 0) s.p01 = s.w4[0] * s.w4[1];
+      else if constexpr (a == 1) s.p23 = s.w4[2] * s.w4[3];
+      else s.wp = s.p01 * s.p23;
+    } else if constexpr (kind == kLog) {
+      s.lg = __builtin_amdgcn_logf(s.wp);
+    } else if constexpr (kind == kEi) {
+      s.e_inc = kLn2 * (s.lg - 16.f);
+    } else if constexpr (kind == kCmp) {
+      s.slow = !(s.wp <= kFastProd);
+    } else if constexpr (kind == kRc) {
+      s.w[a] = __builtin_amdgcn_rcpf(s.w[a]);
+    } else if constexpr (kind == kS) {
+      c[a] = s.w[a] - 0.5f;
+    }
+  }
+  template <int I, int E>
+  __device__ static inline void ops(const f32x16& z, float* c, EpiState& s) {
+    if constexpr (I < E) {
+      op<tbl.op[I]>(z, c, s);
+      ops<I + 1, E>(z, c, s);
+    }
+  }
+  __device__ static inline void pre(const f32x16& z, float* c, EpiState& s) { ops<0, tbl.npre>(z, c, s); }
+  template <int J>
+  __device__ static inline void slot(const f32x16& z, float* c, EpiState& s) {
+    ops<tbl.start[J], tbl.start[J + 1]>(z, c, s);
+  }
+  __device__ static inline void all(const f32x16& z, float* c, EpiState& s) { ops<0, tbl.n>(z, c, s); }
+};
+
+// ---------------------------------------------------------------------------------------------------------
+// Interleaved step engine for bf16 operands with D <= 128 (8 waves per workgroup, two per SIMD).
+//
+// With two waves per SIMD the matrix pipe accepts MFMAs from both, so the sweep runs at the MFMA rate only if
+// each wave keeps issuing MFMAs while it does its vector work. Iteration i of a wave therefore issues three
+// mutually independent pieces of work and lets them interleave (the order is pinned with scheduling groups):
+//   - the logit GEMM of step i+1 (A operands read from LDS inside the iteration),
+//   - the gradient GEMM of step i-1 (its G tile packed to bf16 at the start of the iteration),
+//   - the epilogue of step i on the vector ALU, whose logits came from iteration i-1.
+// The loop is unrolled by the ring length (6), so every ring slot and barrier position is a constant: LDS
+// reads use immediate offsets from per-lane base addresses, and the scalar work per iteration is one offset
+// update and the two DMA destinations. Rare work (the |z| form of the forward epilogue, positives of the
+// step) runs in branches after the interleaved block.
+//
+// Rings: the d-packed block of step j (A) is loaded at iteration j - LA into slot j % 6 and read in iteration
+// j - 1; the slot-packed block (B) is loaded at iteration j - LB and read in iteration j + 1. A barrier opens
+// every even iteration and waits for all ring loads but those of the two iterations before it. Then (K = 2
+// iterations per barrier, two iterations of loads in flight): LA >= K + 3 and LB >= K + 1 make every block
+// land before a barrier that precedes its reads, and 6 >= LA + K - 1, 6 >= LB + K + 1 put a barrier between
+// the last read of a slot and its refill.
+// Streamed blocks are addressed through buffer descriptors rebased every 64 steps (offsets stay small for
+// any vocabulary); loads past the end of an array return zeros, whose logits add nothing (z = 0 gives a zero
+// loss term in the signed form and c = 0).
+// ---------------------------------------------------------------------------------------------------------
+template <int D, bool FWD, bool GRAD>
+struct Pipe {
+  static constexpr int NW = 8, KS = D / 16, NDB = D / 32;
+  static constexpr int SB = 32 * D * 2;  // bytes of a 32-row block
+  static constexpr int CPR = D / 8;      // 16-byte chunks per d-packed row
+  static constexpr int K = 2, NR = 6, LA = 5, LB = 3;
+  static constexpr int LOADB = SB / NW >= 1024 ? 16 : 4;  // bytes per lane per DMA instruction
+  static constexpr int WB = 64 * LOADB;
+  static constexpr int NLD = SB / WB / NW;  // DMA instructions per wave and block
+  static constexpr int NRING = GRAD ? 2 : 1;
+  static constexpr int INFL = 2 * NLD * NRING;  // ring loads a barrier leaves in flight (two iterations)
+  static constexpr int RING_B = NR * SB;
+  static constexpr int LDS_BYTES = NRING * NR * SB + NW * 256;
+  static_assert(NLD >= 1 && SB % (WB * NW) == 0, "DMA split");
+  static_assert(LA >= K + 3 && NR >= LA + K - 1 && LB >= K + 1 && NR >= LB + K + 1, "ring constraints");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+  char* lds;
+  uint32_t lds_s;  // LDS byte address of `lds`, wave-uniform
+  int wave, lane;
+  const char* X;     // d-packed streamed operand (E in the forward, Hc in the backward)
+  int64_t x_bytes;   // its size in bytes
+  const char* Xsp;   // slot-packed copy (Evp / Hrp)
+  int64_t xsp_bytes;
+  const int32_t* bptr;
+  const int2* pairs;
+  int64_t bbase;
+  int own0, j0, j1;
+  uint32_t aoff[KS];  // per-lane LDS byte offset of A chunk ks inside slot 0
+  uint32_t boff;      // per-lane LDS byte offset of the B operand inside slot 0 of the B ring
+  uint32_t voffA[NLD], voffB[NLD];
+  __amdgpu_buffer_rsrc_t rA, rB;
+  int soff;
+  // bucket pointers of the current and next 64-step blocks (lane l: step 64b + l), by block parity
+  int bl0, bh0, bl1, bh1;
+  uint64_t nem;  // steps of the current block with a non-empty bucket
+
+  __device__ inline void setup(char* l, int w, int ln) {
+    lds = l;
+    wave = __builtin_amdgcn_readfirstlane(w);
+    lane = ln;
+    lds_s = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void*)l);
+    const int r = ln % 32, h = ln / 32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = r * (D * 2) + (((2 * ks + h) ^ swz<CPR>(r)) * 16);
+    boff = RING_B + ln * 16;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int inst = wave + q * NW;
+      const int pos = inst * WB + ln * LOADB;
+      const int row = pos / (D * 2), within = pos % (D * 2);
+      voffA[q] = row * (D * 2) + (((within / 16) ^ swz<CPR>(row)) * 16) + within % 16;
+      voffB[q] = pos;
+    }
+  }
+  __device__ static inline __amdgpu_buffer_rsrc_t rsrc(const char* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+  }
+  // descriptors for the loads of iterations 64b .. 64b + 63 (soffset = (i - 64b) * SB)
+  __device__ inline void window(int b) {
+    const int64_t a0 = ((int64_t)j0 + 64 * b + LA) * SB, b0 = ((int64_t)j0 + 64 * b + LB) * SB;
+    rA = rsrc(X + a0, x_bytes - a0);
+    if (GRAD) rB = rsrc(Xsp + b0, xsp_bytes - b0);
+    soff = 0;
+  }
+  __device__ inline void dma(__amdgpu_buffer_rsrc_t r, uint32_t ring, int slot, const uint32_t* voff, int so) const {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      lds_void* dst = (lds_void*)(size_t)(lds_s + ring + slot * SB + (wave + q * NW) * WB);
+      if constexpr (LOADB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff[q], so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff[q], so, 0, 0);
+    }
+  }
+  // the loads of iteration i (after the barrier of the iteration, if any)
+  __device__ inline void dma_iter(int sAw, int sBw) {
+    dma(rA, 0, sAw, voffA, soff);
+    if (GRAD) dma(rB, RING_B, sBw, voffB, soff);
+    soff += SB;
+  }
+
+  // bucket pointers of block b (steps 64b .. 64b + 63 of the unit) into lo/hi
+  __device__ inline void bkt_load(int b, int& lo, int& hi) const {
+    int x = j0 + 64 * b + lane;
+    x = x < j1 - 1 ? x : j1 - 1;
+    lo = bptr[bbase + x];
+    hi = bptr[bbase + x + 1];
+  }
+  // at iteration 64b: block b becomes current, block b + 1 is requested, the load window moves
+  __device__ inline void block_start(int b) {
+    if (b & 1) {
+      nem = __builtin_amdgcn_ballot_w64(bl1 != bh1);
+      bkt_load(b + 1, bl0, bh0);
+    } else {
+      nem = __builtin_amdgcn_ballot_w64(bl0 != bh0);
+      bkt_load(b + 1, bl1, bh1);
+    }
+    window(b);
+  }
+
+  __device__ inline bf16x8 rdA(int slot, int ks) const { return *(const bf16x8*)(lds + aoff[ks] + slot * SB); }
+  __device__ inline bf16x8 rdB(int slot, int m) const { return *(const bf16x8*)(lds + boff + slot * SB + m * 1024); }
+
+  __device__ inline f32x16 logits(int slot, const bf16x8* own) const {
+    f32x16 z = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdA(slot, ks), own[ks], z, 0, 0, 0);
+    return z;
+  }
+
+  // positives of step i (its bucket is not empty): mask, then c -= 1 there and (forward) posz += z
+  __device__ inline void positives(int i, const f32x16& z, float* c, float& posz) {
+    const int b = i >> 6;
+    const int lo = (b & 1) ? bl1 : bl0, hi = (b & 1) ? bh1 : bh0;
+    const int pb = __builtin_amdgcn_readlane(lo, i & 63), pe = __builtin_amdgcn_readlane(hi, i & 63);
+    uint32_t* lm = (uint32_t*)(lds + NRING * NR * SB) + wave * 64;
+    const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + i) * 32, FWD, lm, lane);
+    if (pm) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (pm & (1u << q)) {
+          if (FWD) posz += z[q];
+          c[q] -= 1.f;
+        }
+    }
+  }
+
+  // MFMAs of an interleaved iteration: with the gradient GEMM, even j = logit MFMA j/2 of step i+1 and odd
+  // j = gradient MFMA (j-1)/2 of step i-1 (tile (j-1)/4, G half ((j-1)/2) % 2); without it, logit MFMA j.
+  static constexpr int NM = GRAD ? 2 * KS : KS;
+  using ES = EpiOps<FWD, GRAD, NM>;
+  static_assert(!GRAD || KS == 2 * NDB, "logit and gradient MFMAs alternate");
+
+  __device__ inline bf16x8 opnd_read(int j, int sAr, int sBr) const {
+    return GRAD ? ((j & 1) ? rdB(sBr, j >> 1) : rdA(sAr, j >> 1)) : rdA(sAr, j);
+  }
+  // Slot J: MFMA J, its share of the epilogue, and the LDS read of the operand of MFMA J + 3. sched_barrier
+  // keeps the slots in order (the compiler would otherwise issue each read right before its MFMA).
+  template <int J>
+  __device__ inline void slots(int sAr, int sBr, const bf16x8* own, f32x16* acc, f32x16& zn, const f32x16& zc,
+                               float* c, EpiState& st, bf16x8* opnd) const {
+    if constexpr (J < NM) {
+      if constexpr (GRAD && (J & 1))
+        acc[J >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.g[(J >> 1) & 1], opnd[J], acc[J >> 2], 0, 0, 0);
+      else
+        zn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[J], own[GRAD ? J >> 1 : J], zn, 0, 0, 0);
+      ES::template slot<J>(zc, c, st);
+      if constexpr (J + 3 < NM) opnd[J + 3] = opnd_read(J + 3, sAr, sBr);
+      __builtin_amdgcn_sched_barrier(0);
+      slots<J + 1>(sAr, sBr, own, acc, zn, zc, c, st, opnd);
+    }
+  }
+
+  // One iteration (see the struct comment). HASG: the gradient GEMM of step i-1 is due (every iteration but
+  // the first). Slots: sAr / sBr read, sAw / sBw loaded.
+  template <bool HASG>
+  __device__ inline void iter(int i, int sAr, int sBr, int sAw, int sBw, bool bar, const bf16x8* own,
+                              f32x16* acc, f32x16& zc, float* c, float& e_acc, float& posz) {
+    if (bar) {
+      wait_vm_and_barrier<INFL>();
+      if ((i & 63) == 0) block_start(i >> 6);
+    }
+    dma_iter(sAw, sBw);
+    EpiState st;
+    f32x16 zn;
+    if constexpr (HASG || !GRAD) {
+      bf16x8 opnd[NM];
+      opnd[0] = opnd_read(0, sAr, sBr);
+      opnd[1] = opnd_read(1, sAr, sBr);
+      opnd[2] = opnd_read(2, sAr, sBr);
+      ES::pre(zc, c, st);
+      zn = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      slots<0>(sAr, sBr, own, acc, zn, zc, c, st, opnd);
+    } else {
+      zn = logits(sAr, own);
+      ES::all(zc, c, st);
+    }
+    if (FWD) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(st.slow) != 0, 0)) {
+        float dummy = 0.f;
+        st.e_inc = 0.f;
+        epi_rows<GRAD, false, true>(zc, 0u, c, st.e_inc, dummy);
+      }
+      e_acc += st.e_inc;
+    }
+    if (__builtin_expect((nem >> (i & 63)) & 1, 0)) positives(i, zc, c, posz);
+    zc = zn;
+  }
+
+  // Runs the steps [j0, j1) of a unit. own: owner operand; acc: gradient tiles; e_acc / posz: forward row sums.
+  __device__ inline void run(const bf16x8* own, f32x16* acc, float& e_acc, float& posz) {
+    const int n = j1 - j0;
+    if (n <= 0) return;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the previous unit's reads are done
+    {
+      const int64_t a0 = (int64_t)j0 * SB;
+      const __amdgpu_buffer_rsrc_t r0 = rsrc(X + a0, x_bytes - a0);
+#pragma unroll
+      for (int q = 0; q < LA; ++q) dma(r0, 0, q, voffA, q * SB);
+      if (GRAD) {
+        const __amdgpu_buffer_rsrc_t r1 = rsrc(Xsp + a0, xsp_bytes - a0);
+#pragma unroll
+        for (int q = 0; q < LB; ++q) dma(r1, RING_B, q, voffB, q * SB);
+      }
+    }
+    bkt_load(0, bl0, bh0);
+    bkt_load(1, bl1, bh1);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    nem = __builtin_amdgcn_ballot_w64(bl0 != bh0);
+    window(0);
+    f32x16 zc = logits(0, own);
+    float c[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c[q] = 0.f;
+    // iteration 0: logits of step 1, epilogue of step 0 (no gradient yet); it counts as a barrier iteration
+    iter<false>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, e_acc, posz);
+    int i = 1;
+    // iterations 1 + 6m + u: slots A read (2 + u) % 6, B read u, A load u, B load (4 + u) % 6; barrier at odd u
+    for (; i + 5 < n; i += 6) {
+#pragma unroll
+      for (int u = 0; u < 6; ++u)
+        iter<true>(i + u, (2 + u) % NR, u, u, (4 + u) % NR, (u & 1) != 0, own, acc, zc, c, e_acc, posz);
+    }
+    for (; i < n; ++i)
+      iter<true>(i, (i + 1) % NR, (i - 1) % NR, (i + LA) % NR, (i + LB) % NR, (i & 1) == 0, own, acc, zc, c, e_acc,
+                 posz);
+    // iteration n: the gradient GEMM of step n - 1
+    wait_vm_and_barrier<0>();
+    if (GRAD) {
+      bf16x8 g[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) g[q][jj] = (__bf16)c[q * 8 + jj];
+      const int s = (n - 1) % NR;
+#pragma unroll
+      for (int m = 0; m < 2 * NDB; ++m)
+        acc[m / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[m % 2], rdB(s, m), acc[m / 2], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+};
+
+// Whether a sweep instance runs on the interleaved engine (bf16, D = 64 or 128, 8 waves, one pass, no Cut
+// Metrics, no scoring) or on the general one.
+template <typename T, int D, int NW, bool MET, int KT, int PART>
+__host__ __device__ constexpr bool use_pipe() {
+#ifdef CUTBCE_NO_PIPE
+  return false;
+#else
+  return sizeof(T) == 2 && (D == 64 || D == 128) && NW == 8 && !MET && KT == 0 && PART == 0;
+#endif
+}
+template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET, int KT, int PART>
+constexpr size_t sweep_lds() {
+  if constexpr (use_pipe<T, D, NW, MET, KT, PART>())
+    return Pipe<D <= 128 ? D : 128, FWD, GRAD>::LDS_BYTES;
+  else
+    return Geo<T, D, NW, GRAD>::kLdsBytes;
+}
+
 struct RowsArgs {
   const void* Hc;
   const void* E;
@@ -667,22 +1090,44 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int start = (int)(((int64_t)x * U) / 8), cnt = (int)(((int64_t)(x + 1) * U) / 8) - start;
 
+  constexpr bool kPipe = use_pipe<T, D, NW, MET, KT, DHPART>();
+  using PP = Pipe<D <= 128 ? D : 128, true, WITH_DH>;
   EN en;
-  en.setup(lds, wave, lane);
-  en.X = (const T*)a.E;
-  en.Xsp = (const T*)a.Evp;
-  en.nX = a.V;
-  en.bptr = a.bptr;
-  en.pairs = a.pairs;
+  PP pp;
+  if constexpr (kPipe) {
+    pp.setup(lds, wave, lane);
+    pp.X = (const char*)a.E;
+    pp.x_bytes = a.V * (int64_t)D * 2;
+    pp.Xsp = (const char*)a.Evp;
+    pp.xsp_bytes = a.V_pad * (int64_t)D * 2;
+    pp.bptr = a.bptr;
+    pp.pairs = a.pairs;
+  } else {
+    en.setup(lds, wave, lane);
+    en.X = (const T*)a.E;
+    en.Xsp = (const T*)a.Evp;
+    en.nX = a.V;
+    en.bptr = a.bptr;
+    en.pairs = a.pairs;
+  }
 
   for (int idx = slot; idx < cnt; idx += P / 8) {
     const int u = start + idx;
     const int s = u / Tt, t = u % Tt;
-    en.j0 = (int)(((int64_t)s * n_steps) / S);
-    en.j1 = (int)(((int64_t)(s + 1) * n_steps) / S);
+    const int uj0 = (int)(((int64_t)s * n_steps) / S);
+    const int uj1 = (int)(((int64_t)(s + 1) * n_steps) / S);
     const int r_base = t * RW + wave * 32;
-    en.bbase = (int64_t)t * a.n_vs;
-    en.own0 = r_base;
+    if constexpr (kPipe) {
+      pp.j0 = uj0;
+      pp.j1 = uj1;
+      pp.bbase = (int64_t)t * a.n_vs;
+      pp.own0 = r_base;
+    } else {
+      en.j0 = uj0;
+      en.j1 = uj1;
+      en.bbase = (int64_t)t * a.n_vs;
+      en.own0 = r_base;
+    }
 
     typename EL::Op hop[KS];
 #pragma unroll
@@ -696,7 +1141,10 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     TopK<KT ? KT : 1> tk;
     if (KT) tk.init();
 
-    en.run(hop, acc, e_acc, posz, met, &tk);
+    if constexpr (kPipe)
+      pp.run((const bf16x8*)hop, acc, e_acc, posz);
+    else
+      en.run(hop, acc, e_acc, posz, met, &tk);
 
     // unit results: per-row loss parts and the dH partial of this split
     const int64_t urow = (int64_t)u * RW + wave * 32;  // row of the unit-major partial buffers
@@ -751,7 +1199,7 @@ struct ItemsArgs {
   const double* sumH;
   const float* grad_loss;
   void* dE;
-  int64_t V, n_rs;
+  int64_t V, n_rs, R_pad;
   int n_full;        // item tiles swept whole; the tiles after them are swept in two row halves
   float* tailpart;   // [split tile][half][IW][D] fp32 partial sums of the halved tiles
 };
@@ -795,7 +1243,23 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
 
   const int n_valid = a.ctl->n_valid;
   const int n_st = (n_valid + 31) / 32;
-  if (n_st > 0) {
+  constexpr bool kPipe = use_pipe<T, D, NW, false, 0, DEPART>();
+  if (kPipe && n_st > 0) {
+    Pipe<D <= 128 ? D : 128, false, true> pp;
+    pp.setup(lds, wave, lane);
+    pp.X = (const char*)a.Hc;
+    pp.x_bytes = a.R_pad * (int64_t)D * 2;
+    pp.Xsp = (const char*)a.Hrp;
+    pp.xsp_bytes = a.R_pad * (int64_t)D * 2;
+    pp.bptr = a.bptr;
+    pp.pairs = a.pairs;
+    pp.bbase = (int64_t)t * a.n_rs;
+    pp.own0 = (int)v_own0;
+    pp.j0 = split < 0 || part == 0 ? 0 : n_st / 2;
+    pp.j1 = split < 0 || part == 1 ? n_st : n_st / 2;
+    float e_acc = 0.f, posz = 0.f;
+    pp.run((const bf16x8*)eop, acc, e_acc, posz);
+  } else if (n_st > 0) {
     EN en;
     en.setup(lds, wave, lane);
     en.X = (const T*)a.Hc;
@@ -944,10 +1408,11 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
     return hipGetLastError();
   } else {
     constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
+    const size_t sm1 = sweep_lds<T, D, NW, true, WITH_DH, MET, KT, 0>();
     int per_cu = 1;
-    hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
+    hipError_t e = kernel_setup<kern>(NW * 64, sm1, per_cu);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm, st, a);
+    hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm1, st, a);
     return hipGetLastError();
   }
 }
@@ -968,7 +1433,9 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   a.dE = dE;
   a.V = L.V;
   a.n_rs = L.n_rs;
-  const size_t sm = G::kLdsBytes;
+  a.R_pad = L.R_pad;
+  const size_t sm = two_pass<T, D>() && sizeof(T) == 4 ? G::kLdsBytes
+                                                        : sweep_lds<T, D, NW, false, true, false, 0, 0>();
   // Two passes (see two_pass) run on the same grid and tail split. Measured: f32 D = 256 (the single pass
   // spills ~300 registers) 8.3 vs 21 ms; bf16 D = 512 (~100 spilled) is faster in one pass, 1.87 vs 2.03 ms.
   constexpr bool kTwoPass = two_pass<T, D>() && sizeof(T) == 4;
