@@ -8,6 +8,8 @@
 namespace cutbce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -70,7 +72,24 @@ struct Ctl {           // device control block
   int32_t bad_ids;     // ids skipped by the bucketing kernels (out of range)
   int32_t pad0;
   double scale;        // s = 1 / (W * V), W = summed weight of the valid rows (R_v without weights); 0 when W == 0
+  uint32_t hnorm_max;  // bits of max_r ||H[r]|| over the valid rows (a non-negative float), set by the H preparation
+  uint32_t hw_absmax;  // bits of max |w_r H[r][d]| over the valid rows (the f16 gradient operand's scale)
 };
+
+// Shapes whose dE sweep runs the interleaved engine with its gradient GEMM in f16 (bf16 inputs, D = 64 or 128):
+// the slot-packed rows Hrp are stored as f16, scaled by 2^hrp_shift(hw_absmax).
+__host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
+
+// Power of two that brings the largest |w_r H[r][d]| into [2^14, 2^15) (0 when every value is 0), so that the f16
+// copy keeps 11 significant bits for every value within 2^29 of the largest.
+__device__ inline int hrp_shift(uint32_t absmax_bits) {
+  const float m = __uint_as_float(absmax_bits);
+  if (!(m > 0.f)) return 0;
+  int e = 0;
+  (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+  const int k = 15 - e;
+  return k < -120 ? -120 : (k > 120 ? 120 : k);
+}
 
 struct Layout {
   int64_t R, V, nnz;

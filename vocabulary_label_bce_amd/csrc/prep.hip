@@ -122,6 +122,8 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
     ctl->n_valid = nv;
     ctl->splits = 0;
     ctl->bad_ids = 0;
+    ctl->hnorm_max = 0u;
+    ctl->hw_absmax = 0u;
     ctl->scale = W != 0.0 ? 1.0 / (W * (double)V) : 0.0;
   }
 }
@@ -172,11 +174,14 @@ __device__ inline void set_run_w<float>(float& run, const float* tile, const flo
 // H preparation: block = 32 compacted rows. Hc[k] = H[row_of[k]] (0 for padding), Hrp = slot-packed blocks of
 // the weighted rows wc[k] Hc[k] (the B operand of the dE sweep's gradient GEMM, so each row's contribution to
 // dE carries its weight), per-block float64 column sums of the weighted rows (the dE sweep's 1/2 sum_r w_r H[r]).
+// With `stats`, it also raises ctl->hnorm_max to the largest row norm ||H[r]|| and ctl->hw_absmax to the largest
+// |w_r H[r][d]| of the block (unsigned maxima of non-negative float bits, so the result is order-independent).
 // ---------------------------------------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const int32_t* __restrict__ row_of,
                                                 const float* __restrict__ wc, int D, T* __restrict__ Hc,
-                                                T* __restrict__ Hrp, double* __restrict__ sum_part) {
+                                                T* __restrict__ Hrp, double* __restrict__ sum_part,
+                                                Ctl* __restrict__ stats) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
   __shared__ float wt[32];
@@ -209,6 +214,52 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
     double s = 0.0;
     for (int rr = 0; rr < 32; ++rr) s += (double)(float)tile[rr * D + d] * (double)wt[rr];
     sum_part[blockIdx.x * (int64_t)D + d] = s;
+  }
+  if (stats) {
+    // 8 lanes per row: squared norm and largest |w x| of the row, then the block maxima
+    const int rr = tid / 8, sub = tid % 8;
+    float n2 = 0.f, am = 0.f;
+    for (int d = sub; d < D; d += 8) {
+      const float x = (float)tile[rr * D + d];
+      n2 += x * x;
+      am = fmaxf(am, fabsf(x * wt[rr]));
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      n2 += __shfl_xor(n2, o, 64);
+      am = fmaxf(am, __shfl_xor(am, o, 64));
+    }
+    float nr = sqrtf(n2);
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
+      nr = fmaxf(nr, __shfl_xor(nr, o, 64));
+      am = fmaxf(am, __shfl_xor(am, o, 64));
+    }
+    if (lane_id() == 0) {
+      atomicMax(&stats->hnorm_max, __float_as_uint(nr));
+      atomicMax(&stats->hw_absmax, __float_as_uint(am));
+    }
+  }
+}
+
+// The slot-packed weighted rows as f16 for the interleaved dE sweep: Hrp = f16(wc[k] Hc[k] 2^s) with
+// s = hrp_shift(ctl->hw_absmax) (an exact power of two; the sweep multiplies its sums by 2^-s). Block = 32 rows.
+__global__ void __launch_bounds__(256) k_prep_hrp16(const __bf16* __restrict__ Hc, const float* __restrict__ wc,
+                                                    const Ctl* __restrict__ ctl, int D, _Float16* __restrict__ Hrp) {
+  const int tid = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * 32;
+  const int sh = hrp_shift(ctl->hw_absmax);
+  const int runs = (D / 32) * 2 * 64;
+  _Float16* dst = Hrp + k0 * D;
+  for (int q = tid; q < runs; q += 256) {
+    const int lane = q % 64, g = (q / 64) % 2, db = q / 128;
+    f16x8 run;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = acc_pos(g * 8 + j, lane / 32);
+      run[j] = (_Float16)ldexpf((float)Hc[(k0 + row) * D + db * 32 + lane % 32] * wc[k0 + row], sh);
+    }
+    *(f16x8*)(dst + slot_off<__bf16>(D, db, g, lane)) = run;
   }
 }
 
@@ -244,19 +295,27 @@ __global__ void __launch_bounds__(1024) k_sum_parts(const double* __restrict__ p
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st) {
   const int64_t nblk = L.R_pad / 32;
   const size_t sm = (size_t)32 * L.D * L.esz;
+  // the f16 copy for the interleaved dE sweep is written by a second kernel once the scale is known
+  const bool f16rp = want_hrp && hrp_is_f16(L.dtype, L.D);
+  Ctl* ctl = (Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {
     hipLaunchKernelGGL(k_prep_h<__bf16>, dim3((unsigned)nblk), dim3(256), sm, st, (const __bf16*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
-                       (__bf16*)(ws + L.off_Hc),
-                       want_hrp ? (__bf16*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
+                       (__bf16*)(ws + L.off_Hc), want_hrp && !f16rp ? (__bf16*)(ws + L.off_Hrp) : nullptr,
+                       (double*)(ws + L.off_sumH_part), f16rp ? ctl : nullptr);
   } else {
     hipLaunchKernelGGL(k_prep_h<float>, dim3((unsigned)nblk), dim3(256), sm, st, (const float*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
                        (float*)(ws + L.off_Hc),
-                       want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part));
+                       want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part), nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (f16rp) {
+    hipLaunchKernelGGL(k_prep_hrp16, dim3((unsigned)nblk), dim3(256), 0, st, (const __bf16*)(ws + L.off_Hc),
+                       (const float*)(ws + L.off_wc), (const Ctl*)ctl, L.D, (_Float16*)(ws + L.off_Hrp));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
                      (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
   return hipGetLastError();

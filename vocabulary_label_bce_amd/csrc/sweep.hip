@@ -23,6 +23,7 @@
 // The forward sweep also serves full-vocabulary scoring (top-k per row, Section I-E's evaluation) with a
 // running top list per lane in place of the loss epilogue, and can count the Cut Metrics of Section III-D.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -628,33 +629,39 @@ struct Engine {
 // interleaved engine can hand out an equal share of them after each MFMA. The arithmetic is that of epi_rows
 // (forward: w = 1 + e^-z, products over pairs and quads, one reciprocal per quad, log2 of the tile product) and
 // of epi_items (backward: c = 1/(1 + e^-z) - 1/2), in the same association, so both engines give the same bits.
-// CVT packs two c values of the previous step into the bf16 G operand.
 // ---------------------------------------------------------------------------------------------------------
+template <typename GT>
 struct EpiState {
   float w[16], w2[8], w4[4], r4[4], ra[4], rb[4];
   float p01, p23, wp, lg, e_inc;
   bool slow;
-  bf16x8 g[2];
+  GT g[2];  // G tile of the previous step, packed from its c by the kCvt operations
 };
 
-template <bool FWD, bool GRAD, int NSLOT>
+#ifndef CUTBCE_PRE_OPS
+#define CUTBCE_PRE_OPS 0  // epilogue operations issued before the first MFMA of an iteration (with its first reads)
+#endif
+template <bool FWD, bool GRAD, int NSLOT, typename GT = bf16x8, int PRE_EXTRA = CUTBCE_PRE_OPS>
 struct EpiOps {
+  using State = EpiState<GT>;
   enum { kCvt = 0, kT, kE, kW, kM2, kM4, kR, kA, kB, kF, kWp, kLog, kEi, kCmp, kRc, kS };
   struct Tbl {
     short op[128];
     short start[34];
     int n, npre;
   };
-  // Natural order: the first G half is packed before any MFMA (pre-slot), the second half right after; then
-  // pairs of logits through exp, the pair and quad products, and each quad's batch inversion one pair later
-  // (so the reciprocal's latency is covered); the tile product and its log come last.
+  // Natural order: the first half of the previous step's G tile is packed before any MFMA (pre-slot), the second
+  // half right after; then pairs of logits through exp, the pair and quad products, and each quad's batch
+  // inversion one pair later (so the reciprocal's latency is covered); the tile product and its log come last.
+  // (Packing after the iteration's branches instead, with the packed tile carried, measured 2.5% slower in the
+  // forward sweep: there the conversions overlap no MFMA.)
   static constexpr Tbl make() {
     Tbl t{};
     int n = 0;
     auto push = [&](int kind, int arg) { t.op[n++] = (short)(kind * 64 + arg); };
     if (GRAD)
       for (int p = 0; p < 4; ++p) push(kCvt, p);
-    t.npre = n;
+    int npre = n + PRE_EXTRA;
     for (int p = 0; p < 8; ++p) {
       push(kT, 2 * p);
       push(kT, 2 * p + 1);
@@ -697,17 +704,19 @@ struct EpiOps {
       push(kCmp, 0);
     }
     t.n = n;
+    t.npre = npre < n ? npre : n;
     for (int j = 0; j <= NSLOT; ++j) t.start[j] = (short)(t.npre + (n - t.npre) * j / (NSLOT > 0 ? NSLOT : 1));
     return t;
   }
   static constexpr Tbl tbl = make();
 
   template <int OPC>
-  __device__ static inline void op(const f32x16& z, float* c, EpiState& s) {
+  __device__ static inline void op(const f32x16& z, float* c, State& s) {
     constexpr int kind = OPC / 64, a = OPC % 64;
     if constexpr (kind == kCvt) {
-      s.g[a / 4][2 * (a % 4)] = (__bf16)c[2 * a];
-      s.g[a / 4][2 * (a % 4) + 1] = (__bf16)c[2 * a + 1];
+      using E = typename std::conditional<std::is_same<GT, f16x8>::value, _Float16, __bf16>::type;
+      s.g[a / 4][2 * (a % 4)] = (E)c[2 * a];
+      s.g[a / 4][2 * (a % 4) + 1] = (E)c[2 * a + 1];
     } else if constexpr (kind == kT) {
       s.w[a] = z[a] * -kLog2e;
     } else if constexpr (kind == kE) {
@@ -744,18 +753,93 @@ struct EpiOps {
     }
   }
   template <int I, int E>
-  __device__ static inline void ops(const f32x16& z, float* c, EpiState& s) {
+  __device__ static inline void ops(const f32x16& z, float* c, State& s) {
     if constexpr (I < E) {
       op<tbl.op[I]>(z, c, s);
       ops<I + 1, E>(z, c, s);
     }
   }
-  __device__ static inline void pre(const f32x16& z, float* c, EpiState& s) { ops<0, tbl.npre>(z, c, s); }
+  __device__ static inline void pre(const f32x16& z, float* c, State& s) { ops<0, tbl.npre>(z, c, s); }
   template <int J>
-  __device__ static inline void slot(const f32x16& z, float* c, EpiState& s) {
+  __device__ static inline void slot(const f32x16& z, float* c, State& s) {
     ops<tbl.start[J], tbl.start[J + 1]>(z, c, s);
   }
-  __device__ static inline void all(const f32x16& z, float* c, EpiState& s) { ops<0, tbl.n>(z, c, s); }
+  __device__ static inline void all(const f32x16& z, float* c, State& s) { ops<0, tbl.n>(z, c, s); }
+};
+
+// ---------------------------------------------------------------------------------------------------------
+// Polynomial epilogue of the dE sweep for tiles whose logits are known to satisfy |z| <= 1 (the sweep checks the
+// Cauchy-Schwarz bound |H[r].E[v]| <= ||H[r]|| ||E[v]|| per wave): c = sigma(z) - 1/2 = tanh(z/2)/2 as the
+// Taylor polynomial z/4 - z^3/48 + z^5/480 - 17 z^7/80640 (an alternating series: the error is below the first
+// omitted term 31 |z|^9 / 1451520 <= 2.2e-5, relative 1e-4 at |z| = 1 and smaller below), evaluated on packed
+// f16 pairs. It needs no transcendental and writes the f16 G operand directly; its f16 rounding (about 2^-10
+// relative) is finer than the bf16 G of the exact path.
+// ---------------------------------------------------------------------------------------------------------
+struct PolyState {
+  f16x2 zh[8], z2[8], t[8];
+};
+// Largest ||H[r]|| ||E[v]|| (over a wave's items and all rows) for which the polynomial is used; the margin below
+// 1 covers the float32 rounding of the norms and of the logit itself.
+constexpr float kPolyBound = 0.999f;
+
+template <int NSLOT>
+struct EpiPoly {
+  enum { kCz = 1, kZ2, kP3, kP2, kP1, kC };
+  struct Tbl {
+    short op[64];
+    short start[34];
+    int n;
+  };
+  static constexpr Tbl make() {
+    Tbl t{};
+    int n = 0;
+    auto push = [&](int kind, int arg) { t.op[n++] = (short)(kind * 64 + arg); };
+    for (int p = 0; p < 8; p += 2)
+      for (int kind = kCz; kind <= kC; ++kind) {
+        push(kind, p);
+        push(kind, p + 1);
+      }
+    t.n = n;
+    for (int j = 0; j <= NSLOT; ++j) t.start[j] = (short)(n * j / (NSLOT > 0 ? NSLOT : 1));
+    return t;
+  }
+  static constexpr Tbl tbl = make();
+
+  template <int OPC>
+  __device__ static inline void op(const f32x16& z, PolyState& s, f16x8* gn) {
+    constexpr int kind = OPC / 64, a = OPC % 64;
+    const f16x2 c3 = {(_Float16)(-17.0 / 80640.0), (_Float16)(-17.0 / 80640.0)};
+    const f16x2 c2 = {(_Float16)(1.0 / 480.0), (_Float16)(1.0 / 480.0)};
+    const f16x2 c1 = {(_Float16)(-1.0 / 48.0), (_Float16)(-1.0 / 48.0)};
+    const f16x2 c0 = {(_Float16)0.25, (_Float16)0.25};
+    if constexpr (kind == kCz) {
+      s.zh[a] = f16x2{(_Float16)z[2 * a], (_Float16)z[2 * a + 1]};
+    } else if constexpr (kind == kZ2) {
+      s.z2[a] = s.zh[a] * s.zh[a];
+    } else if constexpr (kind == kP3) {
+      s.t[a] = s.z2[a] * c3 + c2;
+    } else if constexpr (kind == kP2) {
+      s.t[a] = s.z2[a] * s.t[a] + c1;
+    } else if constexpr (kind == kP1) {
+      s.t[a] = s.z2[a] * s.t[a] + c0;
+    } else if constexpr (kind == kC) {
+      const f16x2 c = s.zh[a] * s.t[a];
+      gn[a / 4][2 * (a % 4)] = c[0];
+      gn[a / 4][2 * (a % 4) + 1] = c[1];
+    }
+  }
+  template <int I, int E>
+  __device__ static inline void ops(const f32x16& z, PolyState& s, f16x8* gn) {
+    if constexpr (I < E) {
+      op<tbl.op[I]>(z, s, gn);
+      ops<I + 1, E>(z, s, gn);
+    }
+  }
+  template <int J>
+  __device__ static inline void slot(const f32x16& z, PolyState& s, f16x8* gn) {
+    ops<tbl.start[J], tbl.start[J + 1]>(z, s, gn);
+  }
+  __device__ static inline void all(const f32x16& z, PolyState& s, f16x8* gn) { ops<0, tbl.n>(z, s, gn); }
 };
 
 // ---------------------------------------------------------------------------------------------------------
@@ -777,14 +861,24 @@ struct EpiOps {
 // every even iteration and waits for all ring loads but those of the two iterations before it. Then (K = 2
 // iterations per barrier, two iterations of loads in flight): LA >= K + 3 and LB >= K + 1 make every block
 // land before a barrier that precedes its reads, and 6 >= LA + K - 1, 6 >= LB + K + 1 put a barrier between
-// the last read of a slot and its refill.
+// the last read of a slot and its refill. (Reading an iteration's first operands at the end of the one before,
+// with 8-slot rings, measured 1.5% slower.)
 // Streamed blocks are addressed through buffer descriptors rebased every 64 steps (offsets stay small for
 // any vocabulary); loads past the end of an array return zeros, whose logits add nothing (z = 0 gives a zero
 // loss term in the signed form and c = 0).
 // ---------------------------------------------------------------------------------------------------------
-template <int D, bool FWD, bool GRAD>
+// F16G: the gradient GEMM runs on f16 operands (G and the slot-packed rows, which the H preparation stores as
+// f16 scaled by a power of two); used by the dE sweep, whose tiles can then take the polynomial epilogue.
+template <int D, bool FWD, bool GRAD, bool F16G = false>
 struct Pipe {
   static constexpr int NW = 8, KS = D / 16, NDB = D / 32;
+  using GOp = typename std::conditional<F16G, f16x8, bf16x8>::type;  // operands of the gradient GEMM
+  __device__ static inline f32x16 mma_g(GOp a, GOp b, f32x16 c) {
+    if constexpr (F16G)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
   static constexpr int SB = 32 * D * 2;  // bytes of a 32-row block
   static constexpr int CPR = D / 8;      // 16-byte chunks per d-packed row
   static constexpr int K = 2, NR = 6, LA = 5, LB = 3;
@@ -794,7 +888,9 @@ struct Pipe {
   static constexpr int NRING = GRAD ? 2 : 1;
   static constexpr int INFL = 2 * NLD * NRING;  // ring loads a barrier leaves in flight (two iterations)
   static constexpr int RING_B = NR * SB;
-  static constexpr int LDS_BYTES = NRING * NR * SB + NW * 256;
+  static constexpr int BKT = NRING * NR * SB;        // bucket pointers of two 64-step blocks (2 x 128 ints)
+  static constexpr int LMASK = BKT + 2 * 128 * 4;     // per-wave positive masks (64 ints each)
+  static constexpr int LDS_BYTES = LMASK + NW * 256;
   static_assert(NLD >= 1 && SB % (WB * NW) == 0, "DMA split");
   static_assert(LA >= K + 3 && NR >= LA + K - 1 && LB >= K + 1 && NR >= LB + K + 1, "ring constraints");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -815,9 +911,7 @@ struct Pipe {
   uint32_t voffA[NLD], voffB[NLD];
   __amdgpu_buffer_rsrc_t rA, rB;
   int soff;
-  // bucket pointers of the current and next 64-step blocks (lane l: step 64b + l), by block parity
-  int bl0, bh0, bl1, bh1;
-  uint64_t nem;  // steps of the current block with a non-empty bucket
+  uint64_t nem;  // steps of the current 64-step block whose bucket of positives is not empty
 
   __device__ inline void setup(char* l, int w, int ln) {
     lds = l;
@@ -865,27 +959,29 @@ struct Pipe {
     soff += SB;
   }
 
-  // bucket pointers of block b (steps 64b .. 64b + 63 of the unit) into lo/hi
-  __device__ inline void bkt_load(int b, int& lo, int& hi) const {
-    int x = j0 + 64 * b + lane;
-    x = x < j1 - 1 ? x : j1 - 1;
-    lo = bptr[bbase + x];
-    hi = bptr[bbase + x + 1];
-  }
-  // at iteration 64b: block b becomes current, block b + 1 is requested, the load window moves
-  __device__ inline void block_start(int b) {
-    if (b & 1) {
-      nem = __builtin_amdgcn_ballot_w64(bl1 != bh1);
-      bkt_load(b + 1, bl0, bh0);
-    } else {
-      nem = __builtin_amdgcn_ballot_w64(bl0 != bh0);
-      bkt_load(b + 1, bl1, bh1);
+  // Bucket pointers of block b (steps 64b .. 64b + 63 of the unit: entries j0 + 64b .. j0 + 64b + 64 of bptr,
+  // the last step's end included) go to LDS buffer b & 1 by DMA (waves 0 and 1, 64 entries each; entries past
+  // the unit's end j1 read as 0 and are never used). A block is loaded 64 steps before it is needed, so no
+  // register waits for the load.
+  __device__ inline void bkt_dma(int b) const {
+    if (wave < 2) {
+      const int64_t first = (int64_t)j0 + 64 * b + 64 * wave;
+      const int64_t cnt = (int64_t)j1 + 1 - first;
+      const __amdgpu_buffer_rsrc_t r = rsrc((const char*)(bptr + bbase + first), cnt * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(size_t)(lds_s + BKT + (b & 1) * 512 + wave * 256), 4,
+                                               lane * 4, 0, 0, 0);
     }
+  }
+  __device__ inline const int* bkt(int b) const { return (const int*)(lds + BKT) + (b & 1) * 128; }
+  // At iteration 64b (a barrier iteration, after the barrier): block b is current and the load window moves.
+  __device__ inline void block_start(int b) {
+    const int* k = bkt(b);
+    nem = __builtin_amdgcn_ballot_w64(k[lane] != k[lane + 1]);
     window(b);
   }
 
   __device__ inline bf16x8 rdA(int slot, int ks) const { return *(const bf16x8*)(lds + aoff[ks] + slot * SB); }
-  __device__ inline bf16x8 rdB(int slot, int m) const { return *(const bf16x8*)(lds + boff + slot * SB + m * 1024); }
+  __device__ inline GOp rdB(int slot, int m) const { return *(const GOp*)(lds + boff + slot * SB + m * 1024); }
 
   __device__ inline f32x16 logits(int slot, const bf16x8* own) const {
     f32x16 z = f32x16{};
@@ -894,13 +990,24 @@ struct Pipe {
     return z;
   }
 
+  __device__ inline uint32_t step_mask(int i) {
+    const int* k = bkt(i >> 6);
+    const int pb = __builtin_amdgcn_readfirstlane(k[i & 63]), pe = __builtin_amdgcn_readfirstlane(k[(i & 63) + 1]);
+    uint32_t* lm = (uint32_t*)(lds + LMASK) + wave * 64;
+    return positive_mask(pairs, pb, pe, own0, (j0 + i) * 32, FWD, lm, lane);
+  }
+  // positives of step i on a packed f16 G tile: 1 subtracted at each positive
+  __device__ inline void positives_f16(int i, f16x8* g) {
+    const uint32_t pm = step_mask(i);
+    if (pm) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (pm & (1u << q)) g[q / 8][q % 8] -= (_Float16)1.0f;
+    }
+  }
   // positives of step i (its bucket is not empty): mask, then c -= 1 there and (forward) posz += z
   __device__ inline void positives(int i, const f32x16& z, float* c, float& posz) {
-    const int b = i >> 6;
-    const int lo = (b & 1) ? bl1 : bl0, hi = (b & 1) ? bh1 : bh0;
-    const int pb = __builtin_amdgcn_readlane(lo, i & 63), pe = __builtin_amdgcn_readlane(hi, i & 63);
-    uint32_t* lm = (uint32_t*)(lds + NRING * NR * SB) + wave * 64;
-    const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + i) * 32, FWD, lm, lane);
+    const uint32_t pm = step_mask(i);
     if (pm) {
 #pragma unroll
       for (int q = 0; q < 16; ++q)
@@ -914,53 +1021,92 @@ struct Pipe {
   // MFMAs of an interleaved iteration: with the gradient GEMM, even j = logit MFMA j/2 of step i+1 and odd
   // j = gradient MFMA (j-1)/2 of step i-1 (tile (j-1)/4, G half ((j-1)/2) % 2); without it, logit MFMA j.
   static constexpr int NM = GRAD ? 2 * KS : KS;
-  using ES = EpiOps<FWD, GRAD, NM>;
+#ifndef CUTBCE_READ_AHEAD
+#define CUTBCE_READ_AHEAD 3
+#endif
+  static constexpr int RA = CUTBCE_READ_AHEAD;  // MFMAs between an operand's LDS read and its use
+  using ES = EpiOps<FWD, GRAD, NM, GOp>;
   static_assert(!GRAD || KS == 2 * NDB, "logit and gradient MFMAs alternate");
 
   __device__ inline bf16x8 opnd_read(int j, int sAr, int sBr) const {
-    return GRAD ? ((j & 1) ? rdB(sBr, j >> 1) : rdA(sAr, j >> 1)) : rdA(sAr, j);
+    return GRAD ? ((j & 1) ? __builtin_bit_cast(bf16x8, rdB(sBr, j >> 1)) : rdA(sAr, j >> 1)) : rdA(sAr, j);
   }
-  // Slot J: MFMA J, its share of the epilogue, and the LDS read of the operand of MFMA J + 3. sched_barrier
+  // Slot J: MFMA J, its share of the epilogue, and the LDS read of the operand of MFMA J + RA. sched_barrier
   // keeps the slots in order (the compiler would otherwise issue each read right before its MFMA).
-  template <int J>
+  // POLY: the polynomial epilogue (writes the next G tile gn; the gradient MFMAs use the carried g) instead of
+  // the exact one (packs the carried c of the previous step into st.g for the gradient MFMAs, writes the new c).
+  template <int J, bool POLY>
   __device__ inline void slots(int sAr, int sBr, const bf16x8* own, f32x16* acc, f32x16& zn, const f32x16& zc,
-                               float* c, EpiState& st, bf16x8* opnd) const {
+                               float* c, typename ES::State& st, PolyState& ps, const GOp* g, GOp* gn,
+                               bf16x8* opnd) const {
     if constexpr (J < NM) {
       if constexpr (GRAD && (J & 1))
-        acc[J >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.g[(J >> 1) & 1], opnd[J], acc[J >> 2], 0, 0, 0);
+        acc[J >> 2] = mma_g((POLY ? g : st.g)[(J >> 1) & 1], __builtin_bit_cast(GOp, opnd[J]), acc[J >> 2]);
       else
         zn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[J], own[GRAD ? J >> 1 : J], zn, 0, 0, 0);
-      ES::template slot<J>(zc, c, st);
-      if constexpr (J + 3 < NM) opnd[J + 3] = opnd_read(J + 3, sAr, sBr);
+      if constexpr (POLY)
+        EpiPoly<NM>::template slot<J>(zc, ps, gn);
+      else
+        ES::template slot<J>(zc, c, st);
+      if constexpr (J + RA < NM) opnd[J + RA] = opnd_read(J + RA, sAr, sBr);
       __builtin_amdgcn_sched_barrier(0);
-      slots<J + 1>(sAr, sBr, own, acc, zn, zc, c, st, opnd);
+      slots<J + 1, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, g, gn, opnd);
     }
   }
 
   // One iteration (see the struct comment). HASG: the gradient GEMM of step i-1 is due (every iteration but
   // the first). Slots: sAr / sBr read, sAw / sBw loaded.
-  template <bool HASG>
+  __device__ static inline void pack(const float* c, GOp* g) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if constexpr (F16G)
+          g[q][jj] = (_Float16)c[q * 8 + jj];
+        else
+          g[q][jj] = (__bf16)c[q * 8 + jj];
+      }
+  }
+
+  // The previous step's G tile is carried in c (exact epilogue: float values, packed inside the iteration) or in
+  // g (polynomial epilogue: packed f16); on return they hold step i's.
+  // POLY (dE sweep with F16G only): the polynomial epilogue.
+  template <bool HASG, bool POLY>
   __device__ inline void iter(int i, int sAr, int sBr, int sAw, int sBw, bool bar, const bf16x8* own,
-                              f32x16* acc, f32x16& zc, float* c, float& e_acc, float& posz) {
+                              f32x16* acc, f32x16& zc, float* c, GOp* g, float& e_acc, float& posz) {
+    static_assert(!POLY || (F16G && !FWD && GRAD), "polynomial epilogue: f16 dE sweep only");
+    const bool newblk = bar && (i & 63) == 0;
     if (bar) {
       wait_vm_and_barrier<INFL>();
-      if ((i & 63) == 0) block_start(i >> 6);
+      if (newblk) block_start(i >> 6);
     }
     dma_iter(sAw, sBw);
-    EpiState st;
+    if (newblk) bkt_dma((i >> 6) + 1);  // after the ring loads: the next barrier waits for nothing extra
+    typename ES::State st;
+    PolyState ps;
+    GOp gn[2];
     f32x16 zn;
     if constexpr (HASG || !GRAD) {
       bf16x8 opnd[NM];
-      opnd[0] = opnd_read(0, sAr, sBr);
-      opnd[1] = opnd_read(1, sAr, sBr);
-      opnd[2] = opnd_read(2, sAr, sBr);
-      ES::pre(zc, c, st);
+#pragma unroll
+      for (int j = 0; j < RA; ++j) opnd[j] = opnd_read(j, sAr, sBr);
+      if constexpr (!POLY) ES::pre(zc, c, st);
       zn = f32x16{};
       __builtin_amdgcn_sched_barrier(0);
-      slots<0>(sAr, sBr, own, acc, zn, zc, c, st, opnd);
+      slots<0, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, g, gn, opnd);
     } else {
       zn = logits(sAr, own);
-      ES::all(zc, c, st);
+      if constexpr (POLY)
+        EpiPoly<NM>::all(zc, ps, gn);
+      else
+        ES::all(zc, c, st);
+    }
+    if constexpr (POLY) {
+      if (__builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
+      g[0] = gn[0];
+      g[1] = gn[1];
+      zc = zn;
+      return;
     }
     if (FWD) {
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(st.slow) != 0, 0)) {
@@ -975,6 +1121,7 @@ struct Pipe {
   }
 
   // Runs the steps [j0, j1) of a unit. own: owner operand; acc: gradient tiles; e_acc / posz: forward row sums.
+  template <bool POLY = false>
   __device__ inline void run(const bf16x8* own, f32x16* acc, float& e_acc, float& posz) {
     const int n = j1 - j0;
     if (n <= 0) return;
@@ -990,39 +1137,34 @@ struct Pipe {
         for (int q = 0; q < LB; ++q) dma(r1, RING_B, q, voffB, q * SB);
       }
     }
-    bkt_load(0, bl0, bh0);
-    bkt_load(1, bl1, bh1);
+    bkt_dma(0);
+    bkt_dma(1);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    nem = __builtin_amdgcn_ballot_w64(bl0 != bh0);
-    window(0);
+    block_start(0);
     f32x16 zc = logits(0, own);
-    float c[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) c[q] = 0.f;
+    float c[16];  // G tile of the last epilogue (exact epilogue)
+    GOp g[2];     // the same, packed (polynomial epilogue)
     // iteration 0: logits of step 1, epilogue of step 0 (no gradient yet); it counts as a barrier iteration
-    iter<false>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, e_acc, posz);
+    // (the one before the loop)
+    iter<false, POLY>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, g, e_acc, posz);
     int i = 1;
     // iterations 1 + 6m + u: slots A read (2 + u) % 6, B read u, A load u, B load (4 + u) % 6; barrier at odd u
-    for (; i + 5 < n; i += 6) {
+    for (; i + NR - 1 < n; i += NR) {
 #pragma unroll
-      for (int u = 0; u < 6; ++u)
-        iter<true>(i + u, (2 + u) % NR, u, u, (4 + u) % NR, (u & 1) != 0, own, acc, zc, c, e_acc, posz);
+      for (int u = 0; u < NR; ++u)
+        iter<true, POLY>(i + u, (2 + u) % NR, u, (1 + LA + u) % NR, (1 + LB + u) % NR, (u & 1) != 0, own, acc, zc, c,
+                         g, e_acc, posz);
     }
     for (; i < n; ++i)
-      iter<true>(i, (i + 1) % NR, (i - 1) % NR, (i + LA) % NR, (i + LB) % NR, (i & 1) == 0, own, acc, zc, c, e_acc,
-                 posz);
+      iter<true, POLY>(i, (i + 1) % NR, (i - 1) % NR, (i + LA) % NR, (i + LB) % NR, (i & 1) == 0, own, acc, zc, c, g,
+                       e_acc, posz);
     // iteration n: the gradient GEMM of step n - 1
     wait_vm_and_barrier<0>();
     if (GRAD) {
-      bf16x8 g[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) g[q][jj] = (__bf16)c[q * 8 + jj];
+      if constexpr (!POLY) pack(c, g);
       const int s = (n - 1) % NR;
 #pragma unroll
-      for (int m = 0; m < 2 * NDB; ++m)
-        acc[m / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[m % 2], rdB(s, m), acc[m / 2], 0, 0, 0);
+      for (int m = 0; m < 2 * NDB; ++m) acc[m / 2] = mma_g(g[m % 2], rdB(s, m), acc[m / 2]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
@@ -1032,16 +1174,12 @@ struct Pipe {
 // Metrics, no scoring) or on the general one.
 template <typename T, int D, int NW, bool MET, int KT, int PART>
 __host__ __device__ constexpr bool use_pipe() {
-#ifdef CUTBCE_NO_PIPE
-  return false;
-#else
   return sizeof(T) == 2 && (D == 64 || D == 128) && NW == 8 && !MET && KT == 0 && PART == 0;
-#endif
 }
 template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET, int KT, int PART>
 constexpr size_t sweep_lds() {
   if constexpr (use_pipe<T, D, NW, MET, KT, PART>())
-    return Pipe<D <= 128 ? D : 128, FWD, GRAD>::LDS_BYTES;
+    return Pipe<D <= 128 ? D : 128, FWD, GRAD, !FWD>::LDS_BYTES;
   else
     return Geo<T, D, NW, GRAD>::kLdsBytes;
 }
@@ -1245,7 +1383,8 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   const int n_st = (n_valid + 31) / 32;
   constexpr bool kPipe = use_pipe<T, D, NW, false, 0, DEPART>();
   if (kPipe && n_st > 0) {
-    Pipe<D <= 128 ? D : 128, false, true> pp;
+    static_assert(!kPipe || hrp_is_f16(1, D), "the interleaved dE sweep reads f16 slot-packed rows");
+    Pipe<D <= 128 ? D : 128, false, true, true> pp;
     pp.setup(lds, wave, lane);
     pp.X = (const char*)a.Hc;
     pp.x_bytes = a.R_pad * (int64_t)D * 2;
@@ -1258,7 +1397,23 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
     pp.j0 = split < 0 || part == 0 ? 0 : n_st / 2;
     pp.j1 = split < 0 || part == 1 ? n_st : n_st / 2;
     float e_acc = 0.f, posz = 0.f;
-    pp.run((const bf16x8*)eop, acc, e_acc, posz);
+    // |z| <= ||H[r]|| ||E[v]|| <= 1 for every logit of this wave: the polynomial epilogue applies
+    float n2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (float)((const bf16x8*)eop)[ks][j];
+        n2 += x * x;
+      }
+    n2 += __shfl_xor(n2, 32, 64);  // the two halves of the item's row
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
+    const float bound = sqrtf(n2) * __uint_as_float(a.ctl->hnorm_max);
+    if (__builtin_amdgcn_readfirstlane(bound <= kPolyBound ? 1 : 0))
+      pp.template run<true>((const bf16x8*)eop, acc, e_acc, posz);
+    else
+      pp.template run<false>((const bf16x8*)eop, acc, e_acc, posz);
   } else if (n_st > 0) {
     EN en;
     en.setup(lds, wave, lane);
@@ -1283,9 +1438,10 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
     return;
   }
 
-  // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d])
+  // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d]); the f16 gradient GEMM summed rows scaled by 2^shift
   const double sc = a.ctl->scale * (double)a.grad_loss[0];
   const float scf = (float)sc;
+  const float unscale = kPipe ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax)) : 1.f;
   T* __restrict__ dE = (T*)a.dE;
 #pragma unroll
   for (int db = 0; db < NDBE; ++db) {
@@ -1294,7 +1450,7 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t v = v_own0 + acc_pos(i, lane / 32);
-      if (v < a.V) dE[v * D + d] = (T)(scf * (acc[db][i] + half));
+      if (v < a.V) dE[v * D + d] = (T)(scf * (acc[db][i] * unscale + half));
     }
   }
 }
@@ -1312,7 +1468,9 @@ __global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
   const float scf = (float)(a.ctl->scale * (double)a.grad_loss[0]);
   const float4 p0 = *(const float4*)(a.tailpart + (int64_t)(split * 2) * IW * D + e);
   const float4 p1 = *(const float4*)(a.tailpart + (int64_t)(split * 2 + 1) * IW * D + e);
-  const float q[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+  // partial sums of the interleaved f16 sweep are in units of 2^-shift
+  const float us = use_pipe<T, D, IW / 32, false, 0, 0>() ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax)) : 1.f;
+  const float q[4] = {(p0.x + p1.x) * us, (p0.y + p1.y) * us, (p0.z + p1.z) * us, (p0.w + p1.w) * us};
   T* __restrict__ out = (T*)a.dE + v * D + d;
 #pragma unroll
   for (int k = 0; k < 4; ++k) out[k] = (T)(scf * (q[k] + (float)(0.5 * a.sumH[d + k])));
