@@ -37,7 +37,8 @@ def build(plant: int = 0, force: bool = False) -> str:
         return out
     os.makedirs(_BUILD, exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", f"-DORACLE_PLANT={plant}",
+    # -std=c99 keeps floating-point contraction off: every product and sum is rounded as written
+    cmd = ["gcc", "-O3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c99", f"-DORACLE_PLANT={plant}",
            _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True, capture_output=True)
     os.replace(tmp, out)

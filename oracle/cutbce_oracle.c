@@ -68,9 +68,23 @@ static double load_elem(const void *p, int dtype, size_t i) {
     return (double)f;
 }
 
+static double bf16_bits_to_double(uint16_t h) {
+    uint32_t bits = ((uint32_t)h) << 16; /* bfloat16 = top half of a float32 */
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* z = sum_d H[r][d] * E[v][d], d ascending (one loop per element type; the same products and additions). */
 static double dot_rv(const void *H, const void *E, int dtype, int64_t r, int64_t v, int D) {
     double z = 0.0;
-    for (int d = 0; d < D; ++d) z += load_elem(H, dtype, (size_t)r * D + d) * load_elem(E, dtype, (size_t)v * D + d);
+    if (dtype == 0) {
+        const float *h = (const float *)H + (size_t)r * D, *e = (const float *)E + (size_t)v * D;
+        for (int d = 0; d < D; ++d) z += (double)h[d] * (double)e[d];
+    } else {
+        const uint16_t *h = (const uint16_t *)H + (size_t)r * D, *e = (const uint16_t *)E + (size_t)v * D;
+        for (int d = 0; d < D; ++d) z += bf16_bits_to_double(h[d]) * bf16_bits_to_double(e[d]);
+    }
     return z;
 }
 

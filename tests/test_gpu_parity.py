@@ -197,65 +197,44 @@ def test_validate_targets_counts_bad_ids():
     assert bad.item() == 2
 
 
-def _sampled(name, n_rows=16, n_items=128, seed=0):
-    """Full-size configuration: GPU outputs vs the oracle on sampled rows and items (same launch shapes
-    as the benchmark)."""
-    cfg = W.CONFIGS[name]
-    p = W.make_problem(cfg, device="cuda")
-    w = Workspace(p["H"], p["E"], p["item_ids"], want_row_loss=True, save_dh=True)
-    g = torch.tensor([1.0], device="cuda")
-    w.forward(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"])
-    dH, dE = w.backward(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], grad=g)
+def test_de_polynomial_and_exact_waves_side_by_side():
+    """The dE sweep's waves choose their epilogue from the bound ||H[r]|| ||E[v]|| <= 1 on their 32 items. Here
+    item blocks alternate between norms well inside the bound (polynomial), just inside it (|z| close to 1, the
+    edge of the polynomial's range) and beyond it (exact form), in one call, with positives everywhere."""
+    R, V, D = 300, 32 * 24, 128
+    p = W.custom_problem(R, V, D, dtype="bf16", seed=71, h_std=1.0, e_std=1.0, pos_per_row=(1, 12),
+                         mask_frac=0.1)
+    H = p["H"].float()
+    H = H / H.norm(dim=1, keepdim=True)  # unit rows: the bound is the item norm
+    E = p["E"].float()
+    E = E / E.norm(dim=1, keepdim=True)
+    target = torch.tensor([0.3, 0.97, 2.5])[torch.arange(V) // 32 % 3].unsqueeze(1)
+    E = E * target
+    # rows aligned with the first item of each 'edge' block give |z| near the bound
+    for b in range(1, V // 32, 3):
+        E[32 * b] = 0.97 * H[(5 * b) % R]
+    p["H"], p["E"] = H.to(torch.bfloat16), E.to(torch.bfloat16)
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=1.25)
+    _check(p, _run(p, g=1.25), ref)
+
+
+@pytest.mark.parametrize("h_scale", [1e-5, 3e3])
+def test_de_f16_operand_scaling(h_scale):
+    """The f16 copy of the rows used by the dE sweep is scaled by a power of two chosen from max |w H|: tiny and
+    large H must come back at full accuracy (weights included)."""
+    p = W.custom_problem(256, 2000, 128, dtype="bf16", seed=72, h_std=h_scale, e_std=0.02, pos_per_row=(1, 6),
+                         mask_frac=0.2)
+    w = torch.linspace(0.25, 3.0, 256)
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.5, row_weight=w)
+    d = _dev(p)
+    ws = Workspace(d["H"], d["E"], d["item_ids"], want_row_loss=True, save_dh=True)
+    ws.forward(d["H"], d["E"], d["row_offsets"], d["item_ids"], d["row_mask"], row_weight=w.cuda())
+    dH, dE = ws.backward(d["H"], d["E"], d["row_offsets"], d["item_ids"], d["row_mask"],
+                         grad=torch.tensor([0.5], device="cuda"), row_weight=w.cuda())
     torch.cuda.synchronize()
-    cpu = {k: v.cpu() for k, v in p.items() if torch.is_tensor(v)}
-    m = cpu["row_mask"].numpy()
-    valid = np.flatnonzero(m)
-    rng = np.random.default_rng(seed)
-    rows = np.concatenate([rng.choice(valid, size=min(n_rows, valid.size), replace=False),
-                           np.flatnonzero(m == 0)[:2]])
-    ids = cpu["item_ids"].numpy()
-    hot = np.bincount(ids, minlength=cfg.V).argsort()[::-1][: n_items // 2] if ids.size else np.zeros(0, int)
-    items = np.unique(np.concatenate([hot, rng.choice(cfg.V, size=n_items // 2, replace=False), [cfg.V - 1]]))
-    ro = oracle.rows(cpu["H"], cpu["E"], cpu["row_offsets"], cpu["item_ids"], cpu["row_mask"], rows)
-    io = oracle.items(cpu["H"], cpu["E"], cpu["row_offsets"], cpu["item_ids"], cpu["row_mask"], items)
-    rl = w.row_loss.double().cpu().numpy()
-    tol = TOL[p["H"].dtype]
-    R_v = valid.size
-    # loss = s * sum of row losses (a property that holds at any size), and sampled row losses match the oracle
-    assert w.loss.item() == pytest.approx(rl.sum() / (R_v * cfg.V), rel=1e-5)
-    np.testing.assert_allclose(rl[rows], ro["row_loss"], rtol=tol["row"], atol=tol["row"] * np.abs(ro["row_loss"]).max())
-    # excess of the sampled rows over V ln 2 (what the logits contribute), up to float32 rounding of row_loss
-    k = min(n_rows, valid.size)
-    ex_ref = ro["row_loss"][:k] - cfg.V * math.log(2.0)
-    ex_got = rl[rows][:k] - cfg.V * math.log(2.0)
-    slack = 8 * float(np.spacing(np.float32(cfg.V * math.log(2.0))))
-    assert np.abs(ex_got - ex_ref).max() <= tol["excess"] * np.abs(ex_ref).max() + slack
-    dHs = dH.double().cpu().numpy()[rows]
-    scale = np.abs(ro["dH"]).max()
-    assert np.abs(dHs - ro["dH"]).max() <= tol["grad"] * scale
-    dEs = dE.double().cpu().numpy()[items]
-    scale = np.abs(io["dE"]).max()
-    assert np.abs(dEs - io["dE"]).max() <= tol["grad"] * scale
-    return w
-
-
-def test_config_v100k_sampled():
-    _sampled("v100k")
-
-
-def test_config_sasrec876k_sampled():
-    _sampled("sasrec876k")
-
-
-def test_config_posdense_sampled():
-    _sampled("posdense", n_rows=8)
-
-
-def test_config_catalog10m_sampled():
-    w = _sampled("catalog10m", n_rows=8, n_items=64)
-    # the workspace never holds a [rows, V] buffer: it is far below the dense logits size
-    cfg = W.CONFIGS["catalog10m"]
-    assert w.ws.numel() < 0.05 * W.dense_logits_bytes(cfg.R, cfg.V)
+    got = dict(loss=ws.loss.item(), row_loss=ws.row_loss.double().cpu().numpy(), dH=dH.double().cpu().numpy(),
+               dE=dE.double().cpu().numpy())
+    _check(p, got, ref, excess=h_scale > 1e-3)
 
 
 def test_malformed_offsets_are_clamped():

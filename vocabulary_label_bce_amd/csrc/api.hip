@@ -51,8 +51,14 @@ Layout make_layout(const cutbce_problem* p) {
   L.n_eblk = (L.V_pad + kEBlkItems - 1) / kEBlkItems;
   L.nb_r = L.n_rt * L.n_vs;
   L.nb_i = L.n_vt * L.n_rs;
-  // forward-sweep partials are indexed by unit: at most max(1024 units, every row tile once) x rows_per_wg
-  const int64_t part_rows = (L.n_rt > 1024 ? L.n_rt : 1024) * (int64_t)L.rows_per_wg;
+  // Forward-sweep partials are indexed by unit (row tile x vocabulary split). The device picks at most
+  // min(64, steps / 8) splits and at most 1024 units (choose_splits), for at most n_rt row tiles; the dE sweep's
+  // halved tail tiles reuse the area (two partial sums each, fewer than min(1024, n_vt) tiles).
+  const int64_t per_tile = L.n_vs / 8 < 1 ? 1 : (L.n_vs / 8 < kMaxSplits ? L.n_vs / 8 : kMaxSplits);
+  int64_t units = L.n_rt * per_tile < 1024 ? L.n_rt * per_tile : 1024;
+  if (units < L.n_rt) units = L.n_rt;
+  const int64_t tail_tiles = L.n_vt < 1024 ? L.n_vt : 1024;
+  const int64_t part_rows = (units > tail_tiles ? units : tail_tiles) * (int64_t)L.rows_per_wg;
   L.part_rows = part_rows;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -86,6 +92,7 @@ Layout make_layout(const cutbce_problem* p) {
   const int64_t nbmax = L.nb_r > L.nb_i ? L.nb_r : L.nb_i;
   L.scan_elems = (size_t)((nbmax + 1 + kScanBlock - 1) / kScanBlock + 1);
   L.off_scan = take(sizeof(int32_t) * L.scan_elems);
+  L.off_cpart = take((sizeof(double) + sizeof(int32_t)) * (size_t)((L.R + 4095) / 4096));  // compaction chunks
   L.total = o;
   return L;
 }

@@ -103,7 +103,7 @@ struct Layout {
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
   size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
-  size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan;
+  size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan, off_cpart;
   size_t scan_elems;
   int64_t part_rows;  // rows of the forward sweep's unit-major partial buffers
   size_t total;

@@ -59,66 +59,104 @@ __device__ inline int block_excl_scan(int v, int* sh, int& total) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Row compaction: one workgroup walks the mask in chunks of 4096 rows (4 consecutive rows per thread), keeping
-// ascending order. Each valid row's weight (1 without weights) goes to wc[k]; their sum W, in float64 (each
-// thread adds its rows in order, then the 1024 partial sums are added in a fixed tree), gives s = 1 / (W V).
+// Row compaction in two passes over chunks of 4096 rows (one workgroup each, 4 consecutive rows per thread):
+//   count  : the chunk's valid rows and the float64 sum of their weights (each thread adds its rows in order,
+//            then a fixed tree over the workgroup);
+//   scatter: the chunk's first compact index is the sum of the counts before it; a workgroup scan then places
+//            every valid row in ascending order: row_of[k], compact_of[r], rptr[k] (the row's id range clamped
+//            into [0, nnz]) and wc[k] = its weight (1 without weights). All chunks clear their share of the
+//            padding entries [R_v, R_pad), and chunk 0 writes R_v and s = 1 / (W V), W = the chunk sums added
+//            in chunk order.
 // ---------------------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ mask,
-                                                  const float* __restrict__ weight,
-                                                  const int32_t* __restrict__ row_offsets, int64_t R,
-                                                  int64_t R_pad, int64_t V, int64_t nnz, Ctl* ctl,
-                                                  int32_t* row_of, int32_t* compact_of, int2* rptr, float* wc) {
+constexpr int kCompactChunk = 4096;
+
+__device__ inline double block_sum_f64(double x, double* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  if (lane_id() == 0) sh[threadIdx.x / 64] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < 16; ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+
+__global__ void __launch_bounds__(1024) k_compact_count(const uint8_t* __restrict__ mask,
+                                                        const float* __restrict__ weight, int64_t R,
+                                                        int32_t* __restrict__ cnt, double* __restrict__ wsum) {
   __shared__ int sh[16];
   __shared__ double shw[16];
-  const int tid = threadIdx.x;
-  int base = 0;
-  double wsum = 0.0;
-  for (int64_t c0 = 0; c0 < R; c0 += 4096) {
-    const int64_t r0 = c0 + 4 * tid;
-    bool f[4];
-    int n = 0;
+  const int64_t r0 = (int64_t)blockIdx.x * kCompactChunk + 4 * threadIdx.x;
+  int n = 0;
+  double w = 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[j] = r0 + j < R && mask[r0 + j] != 0;
-      n += f[j] ? 1 : 0;
+  for (int j = 0; j < 4; ++j)
+    if (r0 + j < R && mask[r0 + j] != 0) {
+      ++n;
+      w += (double)(weight ? weight[r0 + j] : 1.f);
     }
-    int tot;
-    int k = base + block_excl_scan(n, sh, tot);
+  int tot;
+  (void)block_excl_scan(n, sh, tot);
+  const double wt = block_sum_f64(w, shw);
+  if (threadIdx.x == 0) {
+    cnt[blockIdx.x] = tot;
+    wsum[blockIdx.x] = wt;
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_compact_scatter(const uint8_t* __restrict__ mask,
+                                                          const float* __restrict__ weight,
+                                                          const int32_t* __restrict__ row_offsets, int64_t R,
+                                                          int64_t R_pad, int64_t V, int64_t nnz,
+                                                          const int32_t* __restrict__ cnt,
+                                                          const double* __restrict__ wsum, Ctl* ctl,
+                                                          int32_t* row_of, int32_t* compact_of, int2* rptr,
+                                                          float* wc) {
+  __shared__ int sh[16];
+  const int tid = threadIdx.x;
+  const int nchunks = gridDim.x;
+  int base = 0, nv = 0;
+  for (int b = 0; b < nchunks; ++b) {
+    const int c = cnt[b];
+    base += b < (int)blockIdx.x ? c : 0;
+    nv += c;
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * kCompactChunk + 4 * tid;
+  bool f[4];
+  int n = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t r = r0 + j;
-      if (r < R) {
-        if (f[j]) {
-          const float w = weight ? weight[r] : 1.f;
-          wsum += (double)w;
-          wc[k] = w;
-          row_of[k] = (int32_t)r;
-          compact_of[r] = k;
-          // the row's id range, clamped into [0, nnz] (inconsistent offsets give an empty or shortened range)
-          const int64_t b = row_offsets[r] < 0 ? 0 : (row_offsets[r] > nnz ? nnz : row_offsets[r]);
-          const int64_t e = row_offsets[r + 1] < b ? b : (row_offsets[r + 1] > nnz ? nnz : row_offsets[r + 1]);
-          rptr[k] = make_int2((int)b, (int)e);
-          ++k;
-        } else {
-          compact_of[r] = -1;
-        }
+  for (int j = 0; j < 4; ++j) {
+    f[j] = r0 + j < R && mask[r0 + j] != 0;
+    n += f[j] ? 1 : 0;
+  }
+  int tot;
+  int k = base + block_excl_scan(n, sh, tot);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t r = r0 + j;
+    if (r < R) {
+      if (f[j]) {
+        wc[k] = weight ? weight[r] : 1.f;
+        row_of[k] = (int32_t)r;
+        compact_of[r] = k;
+        // the row's id range, clamped into [0, nnz] (inconsistent offsets give an empty or shortened range)
+        const int64_t b = row_offsets[r] < 0 ? 0 : (row_offsets[r] > nnz ? nnz : row_offsets[r]);
+        const int64_t e = row_offsets[r + 1] < b ? b : (row_offsets[r + 1] > nnz ? nnz : row_offsets[r + 1]);
+        rptr[k] = make_int2((int)b, (int)e);
+        ++k;
+      } else {
+        compact_of[r] = -1;
       }
     }
-    base += tot;
   }
-  const int nv = base;
-  for (int64_t k = nv + tid; k < R_pad; k += 1024) {
-    row_of[k] = -1;
-    rptr[k] = make_int2(0, 0);
-    wc[k] = 0.f;
+  for (int64_t q = nv + (int64_t)blockIdx.x * 1024 + tid; q < R_pad; q += (int64_t)nchunks * 1024) {
+    row_of[q] = -1;
+    rptr[q] = make_int2(0, 0);
+    wc[q] = 0.f;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
-  if (lane_id() == 0) shw[tid / 64] = wsum;
-  __syncthreads();
-  if (tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     double W = 0.0;
-    for (int i = 0; i < 16; ++i) W += shw[i];
+    for (int b = 0; b < nchunks; ++b) W += wsum[b];
     ctl->n_valid = nv;
     ctl->splits = 0;
     ctl->bad_ids = 0;
@@ -130,11 +168,19 @@ __global__ void __launch_bounds__(1024) k_compact(const uint8_t* __restrict__ ma
 
 hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const float* weight,
                           const int32_t* row_offsets, hipStream_t st) {
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, weight, row_offsets, L.R, L.R_pad, L.V, L.nnz,
-                     (Ctl*)(ws + L.off_ctl), (int32_t*)(ws + L.off_row_of), (int32_t*)(ws + L.off_compact_of),
-                     (int2*)(ws + L.off_rptr), (float*)(ws + L.off_wc));
+  const int64_t nchunks = (L.R + kCompactChunk - 1) / kCompactChunk;
+  double* wsum = (double*)(ws + L.off_cpart);  // [nchunks] doubles, then [nchunks] ints
+  int32_t* cnt = (int32_t*)(ws + L.off_cpart + sizeof(double) * nchunks);
+  hipLaunchKernelGGL(k_compact_count, dim3((unsigned)nchunks), dim3(1024), 0, st, mask, weight, L.R, cnt, wsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_compact_scatter, dim3((unsigned)nchunks), dim3(1024), 0, st, mask, weight, row_offsets, L.R,
+                     L.R_pad, L.V, L.nnz, (const int32_t*)cnt, (const double*)wsum, (Ctl*)(ws + L.off_ctl),
+                     (int32_t*)(ws + L.off_row_of), (int32_t*)(ws + L.off_compact_of), (int2*)(ws + L.off_rptr),
+                     (float*)(ws + L.off_wc));
   return hipGetLastError();
 }
+
 
 // One slot-packed run (see slot_off) gathered from a [32][D] tile in LDS.
 template <typename T>

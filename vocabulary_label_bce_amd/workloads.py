@@ -12,7 +12,8 @@ Yambda). The Yambda dataset itself is not used: the SASRec-shaped configuration 
 Recipe (the same for every configuration):
   * H and E: float32 normal draws from a seeded ``torch.Generator`` on the generating device, scaled by the
     configured standard deviation, then rounded to bfloat16 by round-to-nearest-even when the configuration
-    is bf16.
+    is bf16. The portable variant (make_dense_portable) draws them with NumPy's PCG64 instead, so that the
+    values do not depend on the host; the full-size parity tests use it with stored reference losses.
   * positives: per valid row a count, then that many *distinct* ids, uniform or from a bounded Zipf law over
     ranks 1..V (id = rank - 1, so id 0 is the hottest item); ids are stored sorted per row.
   * mask: 1 = position is trained, 0 = padding. Masked rows get no positives.
@@ -162,6 +163,23 @@ def make_targets(cfg: WorkloadConfig, seed: int | None = None):
     return mask, row_offsets.astype(np.int32), item_ids.astype(np.int32)
 
 
+def make_dense_portable(cfg: WorkloadConfig, seed: int | None = None):
+    """H [R, D] and E [V, D] on the CPU from NumPy's PCG64 (float32 standard normals by the ziggurat method,
+    scaled, then rounded to bfloat16 when the configuration is bf16): the same values on any host, so values
+    computed once from them (stored reference losses) stay valid wherever the inputs are drawn again."""
+    seed = cfg.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7919])))
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    h_std = cfg.h_std / math.sqrt(cfg.D) if cfg.h_over_sqrt_d else cfg.h_std
+    H = (torch.from_numpy(rng.standard_normal((cfg.R, cfg.D), dtype=np.float32)) * h_std).to(tdt)
+    E = torch.empty(cfg.V, cfg.D, dtype=tdt)
+    slab = max(1, (1 << 26) // cfg.D)
+    for v0 in range(0, cfg.V, slab):
+        v1 = min(cfg.V, v0 + slab)
+        E[v0:v1] = (torch.from_numpy(rng.standard_normal((v1 - v0, cfg.D), dtype=np.float32)) * cfg.e_std).to(tdt)
+    return H, E
+
+
 def make_dense(cfg: WorkloadConfig, seed: int | None = None, device: str | torch.device = "cpu"):
     """H [R, D] and E [V, D] drawn on `device` (torch dtypes float32 or bfloat16)."""
     seed = cfg.seed if seed is None else seed
@@ -180,11 +198,16 @@ def make_dense(cfg: WorkloadConfig, seed: int | None = None, device: str | torch
     return H, E
 
 
-def make_problem(name_or_cfg, seed: int | None = None, device="cpu"):
-    """Full problem as a dict of torch tensors on `device` plus the config."""
+def make_problem(name_or_cfg, seed: int | None = None, device="cpu", portable: bool = False):
+    """Full problem as a dict of torch tensors on `device` plus the config. portable: H and E from
+    make_dense_portable (host-independent values) instead of torch's generator on `device`."""
     cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
     mask, ro, ids = make_targets(cfg, seed)
-    H, E = make_dense(cfg, seed, device)
+    if portable:
+        H, E = make_dense_portable(cfg, seed)
+        H, E = H.to(device), E.to(device)
+    else:
+        H, E = make_dense(cfg, seed, device)
     dev = torch.device(device)
     return dict(
         cfg=cfg,
