@@ -218,11 +218,12 @@ def test_de_polynomial_and_exact_waves_side_by_side():
     _check(p, _run(p, g=1.25), ref)
 
 
-@pytest.mark.parametrize("h_scale", [1e-5, 3e3])
-def test_de_f16_operand_scaling(h_scale):
+@pytest.mark.parametrize("h_scale,D", [(1e-5, 128), (3e3, 128), (1e-5, 512), (3e3, 256)])
+def test_de_f16_operand_scaling(h_scale, D):
     """The f16 copy of the rows used by the dE sweep is scaled by a power of two chosen from max |w H|: tiny and
-    large H must come back at full accuracy (weights included)."""
-    p = W.custom_problem(256, 2000, 128, dtype="bf16", seed=72, h_std=h_scale, e_std=0.02, pos_per_row=(1, 6),
+    large H must come back at full accuracy (weights included), in the interleaved engine (D = 128) and the
+    generic one (D = 256, 512)."""
+    p = W.custom_problem(256, 2000, D, dtype="bf16", seed=72, h_std=h_scale, e_std=0.02, pos_per_row=(1, 6),
                          mask_frac=0.2)
     w = torch.linspace(0.25, 3.0, 256)
     ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.5, row_weight=w)
@@ -235,6 +236,38 @@ def test_de_f16_operand_scaling(h_scale):
     got = dict(loss=ws.loss.item(), row_loss=ws.row_loss.double().cpu().numpy(), dH=dH.double().cpu().numpy(),
                dE=dE.double().cpu().numpy())
     _check(p, got, ref, excess=h_scale > 1e-3)
+
+
+@pytest.mark.parametrize("D,std", [(128, 0.05), (512, 0.03)])
+def test_de_gemm_part_at_items_positive_in_most_rows(D, std):
+    """dE of items that are positives of ~90% of the rows, with small logits: there c = sigma(z) - 1/2 - 1 sits near
+    -1 at most rows, and its rounding in the G tile shows against the GEMM part sum_r (sigma(z) - 1/2) H[r], which
+    is small next to the rank-1 and sparse parts (1/2 sum_r H[r] - sum_{r: v in P_r} H[r]). The GPU must match
+    the oracle to 2e-2 of that part's maximum, plus half a bf16 ulp of each output (2^-8 relative allowed).
+    (A bf16 G tile misses this by 2-6x; the f16 one meets it.)"""
+    R, V = 1024, 1024
+    p = W.custom_problem(R, V, D, dtype="bf16", seed=82, h_std=std, e_std=std, pos_per_row=(1, 4))
+    rng = np.random.default_rng(83)
+    ro = p["row_offsets"].numpy().astype(np.int64)
+    ids = p["item_ids"].numpy()
+    hot = (3, V // 2, V - 1)
+    rows = [np.unique(np.concatenate([ids[ro[r]:ro[r + 1]],
+                                      np.array([v for v in hot if rng.random() < 0.9], dtype=ids.dtype)]))
+            for r in range(R)]
+    p["row_offsets"] = torch.from_numpy(np.concatenate([[0], np.cumsum([x.size for x in rows])]).astype(np.int32))
+    p["item_ids"] = torch.from_numpy(np.concatenate(rows).astype(np.int32))
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=1.0)
+    got = _run(p, g=1.0)
+    _check(p, got, ref)
+    # the GEMM part: the oracle's dE minus s (1/2 sum_r H[r] - Y^T H), all rows valid, g = 1
+    Hd = p["H"].double().numpy()
+    Y = np.zeros((R, V))
+    for r, x in enumerate(rows):
+        Y[r, x] = 1.0
+    rank1_sparse = (0.5 * Hd.sum(0)[None, :] - Y.T @ Hd) / (R * V)
+    gemm = np.abs(ref["dE"] - rank1_sparse).max()
+    excess = np.abs(got["dE"] - ref["dE"]) - (2e-2 * gemm + 2.0 ** -8 * np.abs(ref["dE"]))
+    assert excess.max() <= 0.0, (excess.max() / gemm, gemm)
 
 
 def test_malformed_offsets_are_clamped():

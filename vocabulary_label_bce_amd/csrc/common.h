@@ -76,9 +76,10 @@ struct Ctl {           // device control block
   uint32_t hw_absmax;  // bits of max |w_r H[r][d]| over the valid rows (the f16 gradient operand's scale)
 };
 
-// Shapes whose dE sweep runs the interleaved engine with its gradient GEMM in f16 (bf16 inputs, D = 64 or 128):
-// the slot-packed rows Hrp are stored as f16, scaled by 2^hrp_shift(hw_absmax).
-__host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
+// Shapes whose dE sweep runs its gradient GEMM in f16 (every bf16 input): the slot-packed rows Hrp are stored as
+// f16, scaled by 2^hrp_shift(hw_absmax), and the G tiles c = sigma(z) - 1/2 - y are f16 (c - 1 at a positive
+// keeps 10 fraction bits instead of bf16's 7).
+__host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return dtype == 1 && D > 0; }
 
 // Power of two that brings the largest |w_r H[r][d]| into [2^14, 2^15) (0 when every value is 0), so that the f16
 // copy keeps 11 significant bits for every value within 2^29 of the largest.

@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
   }
 }
 
-// The slot-packed weighted rows as f16 for the interleaved dE sweep: Hrp = f16(wc[k] Hc[k] 2^s) with
+// The slot-packed weighted rows as f16 for the bf16 dE sweep: Hrp = f16(wc[k] Hc[k] 2^s) with
 // s = hrp_shift(ctl->hw_absmax) (an exact power of two; the sweep multiplies its sums by 2^-s). Block = 32 rows.
 __global__ void __launch_bounds__(256) k_prep_hrp16(const __bf16* __restrict__ Hc, const float* __restrict__ wc,
                                                     const Ctl* __restrict__ ctl, int D, _Float16* __restrict__ Hrp) {
@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(1024) k_sum_parts(const double* __restrict__ p
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st) {
   const int64_t nblk = L.R_pad / 32;
   const size_t sm = (size_t)32 * L.D * L.esz;
-  // the f16 copy for the interleaved dE sweep is written by a second kernel once the scale is known
+  // the f16 copy for the bf16 dE sweep is written by a second kernel once the scale is known
   const bool f16rp = want_hrp && hrp_is_f16(L.dtype, L.D);
   Ctl* ctl = (Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {

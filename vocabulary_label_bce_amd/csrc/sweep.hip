@@ -59,6 +59,18 @@ template <> struct GPack<__bf16> {
   }
   __device__ inline bf16x8 op(int q) const { return g[q]; }
 };
+// f16 G tile of the bf16 dE sweep (its B operand, the weighted rows, is f16 scaled by a power of two): three more
+// bits than bf16 for c = sigma(z) - 1/2 - y, which matters at positives, where c lies in [-3/2, -1/2].
+struct GPackF16 {
+  f16x8 g[2];
+  __device__ inline void set(const float* c) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[q][j] = (_Float16)c[q * 8 + j];
+  }
+  __device__ inline f16x8 op(int q) const { return g[q]; }
+};
 template <> struct GPack<float> {
   float g[16];
   __device__ inline void set(const float* c) {
@@ -342,9 +354,11 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // DB0, NDBE: the gradient GEMM covers the d-blocks [DB0, DB0 + NDBE) of the 32-wide blocks of D (acc holds
 // NDBE tiles); LOSS = false skips the loss sums of the forward epilogue (a second pass over the other d-blocks).
 template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int KT = 0, int DB0 = 0,
-          int NDBE = D / 32, bool LOSS = true>
+          int NDBE = D / 32, bool LOSS = true, bool F16G = false>
 struct Engine {
   using EL = Elem<T>;
+  static_assert(!F16G || (std::is_same<T, __bf16>::value && !FWD && GRAD), "f16 G tiles: the bf16 dE sweep");
+  using GP = typename std::conditional<F16G, GPackF16, GPack<T>>::type;
   using G = Geo<T, D, NW, GRAD>;
   static constexpr int KS = D / EL::kK, NDB = D / 32;
   using Op = typename EL::Op;
@@ -466,7 +480,7 @@ struct Engine {
     bkt_init();
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-    GPack<T> g;  // G tile whose gradient GEMM is pending
+    GP g;  // G tile whose gradient GEMM is pending
     if constexpr (kPrefetch) {
       // A operands of the next logit GEMM read a step ahead (they fit in 32 registers per lane); one logit tile
       Op aop[KS];
@@ -515,7 +529,7 @@ struct Engine {
   }
 
   // Iteration i of the larger-D schedule: Z(i+1) into zn, gradient GEMM of step i-1, epilogue of step i (zc).
-  __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GPack<T>& g, f32x16* acc,
+  __device__ inline void step_lds(int i, const Op* own, const f32x16& zc, f32x16& zn, GP& g, f32x16* acc,
                                   float& e_acc, float& posz, int* met, TopK<KT ? KT : 1>* tk) {
     top(i);
     int pb, pe;
@@ -554,22 +568,27 @@ struct Engine {
     return z;
   }
 
-  __device__ inline void grad(int j, const GPack<T>& g, f32x16* acc) const {
+  __device__ inline void grad(int j, const GP& g, f32x16* acc) const {
     grad_slot(j % (G::kNB ? G::kNB : 1), g, acc);
   }
-  __device__ inline void grad_slot(int slot, const GPack<T>& g, f32x16* acc) const {
+  __device__ inline void grad_slot(int slot, const GP& g, f32x16* acc) const {
     const char* b = lds + (G::kNA + slot) * G::kStepBytes;
 #pragma unroll
     for (int db = 0; db < NDBE; ++db)
 #pragma unroll
-      for (int q = 0; q < EL::kGroups; ++q)
-        acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, DB0 + db, q, lane), acc[db]);
+      for (int q = 0; q < EL::kGroups; ++q) {
+        if constexpr (F16G)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              g.op(q), *(const f16x8*)((const T*)b + slot_off<T>(D, DB0 + db, q, lane)), acc[db], 0, 0, 0);
+        else
+          acc[db] = EL::mma(g.op(q), lds_b<T, D>(b, DB0 + db, q, lane), acc[db]);
+      }
   }
 
   // Epilogue of step j (called for j = 0, 1, ... in order): positives of the step (bucket [pb, pe)),
   // loss sums (FWD), the G tile (GRAD) and, with MET, the Cut Metrics counts of the lane: met[0] logits
   // predicted positive (z > 0), met[1] positives predicted positive, met[2] positives.
-  __device__ inline void epilogue(int j, int pb, int pe, const f32x16& z, GPack<T>& g, float& e_acc, float& posz,
+  __device__ inline void epilogue(int j, int pb, int pe, const f32x16& z, GP& g, float& e_acc, float& posz,
                                   int* met, TopK<KT ? KT : 1>* tk) {
     if constexpr (KT > 0) {
       // scoring: keep the lane's best items (real items only; the last step may hold padding). Only the values
@@ -1351,7 +1370,9 @@ template <typename T, int D, int NW, int DEPART = 0>
 __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   using EL = Elem<T>;
   constexpr int NDB = D / 32, NDBE = DEPART ? NDB / 2 : NDB, DB0 = DEPART == 2 ? NDB / 2 : 0;
-  using EN = Engine<T, D, NW, false, true, false, 0, DB0, NDBE>;
+  // bf16: the gradient GEMM takes f16 G tiles and the f16 rows, scaled by 2^s (the sums are unscaled at the end)
+  constexpr bool kF16 = std::is_same<T, __bf16>::value && hrp_is_f16(1, D);
+  using EN = Engine<T, D, NW, false, true, false, 0, DB0, NDBE, true, kF16>;
   constexpr int IW = NW * 32, KS = D / EL::kK;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
@@ -1441,7 +1462,7 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   // dE[v][d] = s * g * (acc + 1/2 sum_r H[r][d]); the f16 gradient GEMM summed rows scaled by 2^shift
   const double sc = a.ctl->scale * (double)a.grad_loss[0];
   const float scf = (float)sc;
-  const float unscale = kPipe ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax)) : 1.f;
+  const float unscale = kF16 ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax)) : 1.f;
   T* __restrict__ dE = (T*)a.dE;
 #pragma unroll
   for (int db = 0; db < NDBE; ++db) {
@@ -1468,8 +1489,9 @@ __global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
   const float scf = (float)(a.ctl->scale * (double)a.grad_loss[0]);
   const float4 p0 = *(const float4*)(a.tailpart + (int64_t)(split * 2) * IW * D + e);
   const float4 p1 = *(const float4*)(a.tailpart + (int64_t)(split * 2 + 1) * IW * D + e);
-  // partial sums of the interleaved f16 sweep are in units of 2^-shift
-  const float us = use_pipe<T, D, IW / 32, false, 0, 0>() ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax)) : 1.f;
+  // partial sums of the f16 gradient GEMM (bf16 inputs) are in units of 2^-shift
+  const float us = std::is_same<T, __bf16>::value && hrp_is_f16(1, D) ? ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax))
+                                                                         : 1.f;
   const float q[4] = {(p0.x + p1.x) * us, (p0.y + p1.y) * us, (p0.z + p1.z) * us, (p0.w + p1.w) * us};
   T* __restrict__ out = (T*)a.dE + v * D + d;
 #pragma unroll
