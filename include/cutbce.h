@@ -101,6 +101,23 @@ cutbce_status cutbce_forward(const cutbce_problem *p, const void *H, const void 
                              const float *row_weight, float *loss, float *row_loss, float *dh_saved,
                              int32_t *metrics, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the scratch array behind cutbce_forward_noalloc (per GPU). */
+#define CUTBCE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* cutbce_forward for callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, computation and outputs as cutbce_forward, except that
+ * the workspace is a device array of the library, CUTBCE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until
+ * the process ends; nothing is allocated. Its device address is looked up on the first call on each device
+ * (hipGetSymbolAddress), so a caller that captures should make one call on the device before capturing.
+ * Errors as for cutbce_forward, and CUTBCE_ERR_WORKSPACE when cutbce_workspace_size() of the problem exceeds
+ * the array (roughly: R * D * 4 * (vocabulary splits, up to 64) plus 2 * V * D + O(R * D + nnz) bytes).
+ * All calls on one GPU share the array and each leaves its contents behind: calls that may overlap on a GPU
+ * (several streams, or several host threads) race and must be serialised by the caller. */
+cutbce_status cutbce_forward_noalloc(const cutbce_problem *p, const void *H, const void *E,
+                                     const int32_t *row_offsets, const int32_t *item_ids,
+                                     const uint8_t *row_mask, const float *row_weight, float *loss,
+                                     float *row_loss, float *dh_saved, int32_t *metrics, void *stream);
+
 /* Backward (Section III-B, Eq. (4); the custom VJP recomputes logit tiles on chip).
  *   row_weight (device) float [R] or NULL: as for cutbce_forward (the same weights as the forward call).
  *   grad_loss (device) float [1]: the cotangent g.

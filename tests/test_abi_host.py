@@ -174,3 +174,18 @@ def test_product_modules_never_import_the_oracle():
             elif isinstance(node, ast.ImportFrom):
                 mods = [node.module or ""]
             assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
+
+
+def test_noalloc_forward_rejects_problems_beyond_its_scratch_before_any_hip_call():
+    """cutbce_forward_noalloc checks the problem and its workspace size against the library's scratch array
+    before it touches the device (fake pointers are never dereferenced)."""
+    lib = B.lib()
+    vp = ctypes.c_void_p
+    big = B.problem(25600, 876000, 70000, 128, B.BF16)
+    assert B.workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    st = lib.cutbce_forward_noalloc(ctypes.byref(big), vp(16), vp(16), vp(16), vp(16), vp(16), None, vp(16), None,
+                                    None, None, None)
+    assert st == 5  # CUTBCE_ERR_WORKSPACE
+    bad = B.problem(0, 100, 0, 128, B.BF16)
+    assert lib.cutbce_forward_noalloc(ctypes.byref(bad), vp(16), vp(16), vp(16), vp(16), vp(16), None, vp(16), None,
+                                      None, None, None) == 2  # CUTBCE_ERR_SHAPE

@@ -30,7 +30,8 @@ class Problem(ctypes.Structure):
                 ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
-EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
+EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_forward_noalloc", "cutbce_backward",
+           "cutbce_validate_targets",
            "cutbce_targets_to_csr", "cutbce_topk",
            "cutbce_profile_enable", "cutbce_profile_read", "cutbce_status_string", "cutbce_version"]
 
@@ -48,6 +49,7 @@ def lib():
         P = ctypes.POINTER(Problem)
         L.cutbce_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
         L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cutbce_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
         L.cutbce_targets_to_csr.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp]
@@ -59,7 +61,8 @@ def lib():
         L.cutbce_status_string.argtypes = [i32]
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
-        for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_backward", "cutbce_validate_targets",
+        for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_forward_noalloc", "cutbce_backward",
+                  "cutbce_validate_targets",
                   "cutbce_targets_to_csr", "cutbce_topk"):
             getattr(L, f).restype = i32
         _lib = L
@@ -109,6 +112,17 @@ def forward(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row_loss, d
     _check(lib().cutbce_forward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
                                 _ptr(row_mask), _ptr(row_weight), _ptr(loss), _ptr(row_loss), _ptr(dh_saved),
                                 _ptr(metrics), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CUTBCE_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row_loss, dh_saved, stream=None,
+                    metrics=None, row_weight=None):
+    """cutbce_forward_noalloc: cutbce_forward with the library's own per-GPU scratch array as workspace."""
+    _check(lib().cutbce_forward_noalloc(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
+                                        _ptr(row_mask), _ptr(row_weight), _ptr(loss), _ptr(row_loss),
+                                        _ptr(dh_saved), _ptr(metrics), _stream(stream)))
 
 
 def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_saved, dH, dE, ws, stream=None,

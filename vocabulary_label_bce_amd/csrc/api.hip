@@ -2,6 +2,7 @@
 // launches for the forward and backward of the fused full-vocabulary BCE.
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/cutbce.h"
@@ -165,6 +166,29 @@ cutbce_status check_common(const cutbce_problem* p, const void* H, const void* E
   return CUTBCE_OK;
 }
 
+// Scratch of cutbce_forward_noalloc: a device array of the library (one per GPU, held until the process ends).
+// In host code `scratch` names a host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed to kernels.
+static __device__ __align__(256) char scratch[CUTBCE_NOALLOC_SCRATCH_BYTES];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+// Device address of the current device's scratch array (looked up on the first call on that device).
+cutbce_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CUTBCE_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return CUTBCE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CUTBCE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CUTBCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,6 +238,21 @@ cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void*
   TRY(timed_rows(L, ws, E, with_dh, metrics != nullptr, st));
   TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, metrics, st));
   return CUTBCE_OK;
+}
+
+cutbce_status cutbce_forward_noalloc(const cutbce_problem* p, const void* H, const void* E,
+                                     const int32_t* row_offsets, const int32_t* item_ids, const uint8_t* row_mask,
+                                     const float* row_weight, float* loss, float* row_loss, float* dh_saved,
+                                     int32_t* metrics, void* stream) {
+  cutbce_status s = check_problem(p);
+  if (s != CUTBCE_OK) return s;
+  if (make_layout(p).total > (size_t)CUTBCE_NOALLOC_SCRATCH_BYTES) return CUTBCE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != CUTBCE_OK) return s;
+  // every kernel of the forward initialises what it reads from the workspace, so the previous call's contents
+  // do not matter
+  return cutbce_forward(p, H, E, row_offsets, item_ids, row_mask, row_weight, loss, row_loss, dh_saved, metrics, ws,
+                        (size_t)CUTBCE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
