@@ -12,6 +12,13 @@ using namespace cutbce;
 
 namespace {
 
+#ifndef CUTBCE_GATHER_POSITIVES
+#define CUTBCE_GATHER_POSITIVES 1
+#endif
+// Where the forward takes its positives (the sparse target correction of the loss and of dH): gathered per row
+// by the finishing kernel (1), or bucketed and folded into the sweep's tiles (0; always so with Cut Metrics).
+constexpr bool kGatherPositives = CUTBCE_GATHER_POSITIVES != 0;
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -136,7 +143,7 @@ void prof_end(ProfRec* r, hipStream_t st) {
 
 hipError_t timed_rows(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
   ProfRec* r = prof_begin(0, st);
-  hipError_t e = launch_rows_sweep(L, ws, E, with_dh, met, st);
+  hipError_t e = launch_rows_sweep(L, ws, E, with_dh, met, !kGatherPositives, st);
   prof_end(r, st);
   return e;
 }
@@ -234,9 +241,11 @@ cutbce_status cutbce_forward(const cutbce_problem* p, const void* H, const void*
   TRY(launch_compact(L, ws, row_mask, row_weight, row_offsets, st));
   TRY(launch_prep_h(L, ws, H, false, st));
   TRY(launch_prep_e(L, ws, E, with_dh, st));
-  TRY(launch_buckets(L, ws, item_ids, true, st));
+  // positives gathered by the finish; the sweep's buckets are empty, or, with Cut Metrics, only counted
+  TRY(kGatherPositives && !metrics ? launch_no_row_buckets(L, ws, st) : launch_buckets(L, ws, item_ids, true, st));
   TRY(timed_rows(L, ws, E, with_dh, metrics != nullptr, st));
-  TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, metrics, st));
+  TRY(launch_rows_finish(L, ws, H, row_mask, loss, row_loss, dh_saved, with_dh, metrics,
+                         kGatherPositives ? E : nullptr, item_ids, st));
   return CUTBCE_OK;
 }
 
@@ -281,9 +290,10 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
     } else {
       float* tmp = (float*)(ws + L.off_dhtmp);
       TRY(launch_prep_e(L, ws, E, true, st));
-      TRY(launch_buckets(L, ws, item_ids, true, st));
+      TRY(kGatherPositives ? launch_no_row_buckets(L, ws, st) : launch_buckets(L, ws, item_ids, true, st));
       TRY(timed_rows(L, ws, E, true, false, st));
-      TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, nullptr, st));
+      TRY(launch_rows_finish(L, ws, H, row_mask, nullptr, nullptr, tmp, true, nullptr,
+                             kGatherPositives ? E : nullptr, item_ids, st));
       TRY(launch_scale_dh(L, tmp, grad_loss, dH, st));
     }
   }

@@ -126,9 +126,17 @@ hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const 
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st);
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st);
 hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st);
-hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st);
+// pos_apply: the positives of the buckets enter the tiles (c - 1 and the sum of their logits); false: with Cut
+// Metrics they are only counted (the finish gathers their terms), without it the buckets are empty anyway.
+hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, bool pos_apply,
+                             hipStream_t st);
+// E != nullptr: the forward sweep ran without positives and the finish gathers them (sum of the positives'
+// logits for the loss, minus the sum of their E rows for dH); E == nullptr: the sweep's partials include them.
 hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
-                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, hipStream_t st);
+                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, const void* E,
+                              const int32_t* item_ids, hipStream_t st);
+// Bucket pointers of the forward sweep set to zero: every bucket empty, the sweep sees no positives.
+hipError_t launch_no_row_buckets(const Layout& L, char* ws, hipStream_t st);
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                               hipStream_t st);
 // full-vocabulary scoring: per-split top-kt lists (kt = kTopKMax entries kept) in the dH partial area

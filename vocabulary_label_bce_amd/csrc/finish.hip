@@ -28,6 +28,68 @@ __device__ inline int wave_sum_i(int x) {
   return x;
 }
 
+// Positives of compact row k gathered here (when the forward sweep ran without them): the row's ids in
+// rptr[k] (clamped range), those in [0, V) and not repeated earlier in the row, give S = sum_{v in P_r} E[v];
+// then sum_{v in P_r} z_rv = H[r] . S (float64) and the sparse part of dH is -S. One wave per row: the lanes form
+// groups of D * sizeof(T) / 16 lanes, each lane loading 16 bytes of an E row; group g takes the positives
+// g, g + NG, ... in row order, and the groups' sums are added in group order (deterministic).
+template <typename T>
+__device__ inline void gather_positives(const int2* __restrict__ rptr, const int32_t* __restrict__ ids,
+                                        const T* __restrict__ E, int64_t V, int D, int64_t k, int lane, float* sh,
+                                        float* S /* [D / 64], d = lane + 64 i */) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte load
+  const int lpr = D / EPL;              // lanes per E row (8 ... 64)
+  const int ng = 64 / lpr, g = lane / lpr, sub = lane % lpr;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  const int2 rg = rptr[k];
+  for (int q0 = rg.x; q0 < rg.y; q0 += 64) {  // uniform
+    const int q = q0 + lane;
+    const int v = q < rg.y ? ids[q] : -1;
+    bool keep = v >= 0 && v < V;
+    // (every lane runs every shuffle: a shuffle reads nothing from lanes that skip it)
+    for (int q1 = rg.x; q1 < q0; q1 += 64) {  // earlier chunks of the row
+      const int u = ids[q1 + lane];           // q1 + 63 < q0 <= rg.y - 1: inside the row
+      for (int j = 0; j < 64; ++j) {
+        const int uj = __shfl(u, j, 64);
+        keep = keep & (uj != v);
+      }
+    }
+    for (int j = 0; j < 63; ++j) {  // earlier lanes of this chunk
+      const int u = __shfl(v, j, 64);
+      keep = keep & !(j < lane && u == v);
+    }
+    uint64_t m = __ballot(keep);
+    while (m) {  // uniform: up to ng positives per round, one per group
+      int src = -1;
+      for (int gg = 0; gg < ng && m; ++gg) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        if (g == gg) src = b;
+      }
+      const int vv = __shfl(v, src < 0 ? 0 : src, 64);
+      if (src >= 0) {
+        const u32x4 raw = *(const u32x4*)(E + (int64_t)vv * D + sub * EPL);
+        const T* x = (const T*)&raw;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += (float)x[e];
+      }
+    }
+  }
+  // the groups' sums, added in group order
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) sh[g * D + sub * EPL + e] = acc[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int i = 0, d = lane; d < D; ++i, d += 64) {
+    float t = 0.f;
+    for (int gg = 0; gg < ng; ++gg) t += sh[gg * D + d];
+    S[i] = t;
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl, const T* __restrict__ H,
                                                      const uint8_t* __restrict__ mask,
@@ -39,7 +101,9 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
                                                      const double* __restrict__ sumE, int64_t R, int64_t V, int D,
                                                      int RW, float* __restrict__ row_loss,
                                                      double* __restrict__ rowloss_c, float* __restrict__ dh_out,
-                                                     int32_t* __restrict__ metrics) {
+                                                     int32_t* __restrict__ metrics, const int2* __restrict__ rptr,
+                                                     const int32_t* __restrict__ ids, const T* __restrict__ E) {
+  __shared__ float sh_pos[4][512];  // per wave: the positive groups' partial sums (at most 512 floats)
   const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = lane_id();
   if (r >= R) return;
@@ -56,11 +120,15 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
   const int t = k / RW, loc = k % RW;
   const double w = (double)wc[k];
   const double sw = ctl->scale * w;  // s w_r (= s exactly for unit weights)
+  float Sp[8];                       // sum of the row's positives' E rows (d = lane + 64 i), gathered here
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Sp[i] = 0.f;
+  if (E) gather_positives<T>(rptr, ids, E, V, D, k, lane, sh_pos[threadIdx.x / 64], Sp);
   if (dh_out) {
-    for (int d = lane; d < D; d += 64) {
+    for (int i = 0, d = lane; d < D; ++i, d += 64) {
       double acc = 0.0;
       for (int s = 0; s < S; ++s) acc += (double)dhpart[((int64_t)(s * Tt + t) * RW + loc) * D + d];
-      dh_out[r * D + d] = (float)(sw * (acc + 0.5 * sumE[d]));
+      dh_out[r * D + d] = (float)(sw * (acc + 0.5 * sumE[d] - (double)Sp[i]));
     }
   }
   double e = 0.0, p = 0.0;
@@ -69,10 +137,14 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
     e += q.x;
     p += q.y;
   }
-  double zs = 0.0;
-  for (int d = lane; d < D; d += 64) zs += (double)(float)H[r * D + d] * sumE[d];
+  double zs = 0.0, pg = 0.0;
+  for (int i = 0, d = lane; d < D; ++i, d += 64) {
+    const double h = (double)(float)H[r * D + d];
+    zs += h * sumE[d];
+    pg += h * (double)Sp[i];
+  }
   e = wave_sum(e);
-  p = wave_sum(p);
+  p = wave_sum(p) + wave_sum(pg);
   zs = wave_sum(zs);
   if (metrics) {
     // Cut Metrics: predicted positive (z > 0), true positives, positives, summed over the splits
@@ -113,7 +185,9 @@ __global__ void __launch_bounds__(1024) k_loss_final(const Ctl* __restrict__ ctl
 }
 
 hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
-                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, hipStream_t st) {
+                              float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, const void* E,
+                              const int32_t* item_ids, hipStream_t st) {
+  const int2* rptr = (const int2*)(ws + L.off_rptr);
   const unsigned blocks = (unsigned)((L.R + 3) / 4);
   const Ctl* ctl = (const Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {
@@ -122,14 +196,16 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
                        (const float*)(ws + L.off_dhpart),
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
-                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);
+                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics, rptr, item_ids,
+                       (const __bf16*)E);
   } else {
     hipLaunchKernelGGL(k_rows_finish<float>, dim3(blocks), dim3(256), 0, st, ctl, (const float*)H, mask,
                        (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_wc),
                        (const float*)(ws + L.off_dhpart),
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
-                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics);
+                       (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics, rptr, item_ids,
+                       (const float*)E);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;

@@ -604,6 +604,10 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   return hipGetLastError();
 }
 
+hipError_t launch_no_row_buckets(const Layout& L, char* ws, hipStream_t st) {
+  return launch_fill_i32((int32_t*)(ws + L.off_bptr_r), L.nb_r + 1, 0, st);
+}
+
 // ---------------------------------------------------------------------------------------------------------
 // Dense padded targets -> CSR ("Cut Binary Cross Entropy", Listing 1 takes targets as [B, N, L] id slots).
 // Row r's ids are targets[r][0..L) in slot order with every slot equal to pad_id dropped.

@@ -374,6 +374,7 @@ struct Engine {
   int64_t bbase;
   int own0;  // first owner index of this wave (compact row or item)
   int j0, j1;
+  bool apply_pos = true;  // false: positives are only counted (Cut Metrics); the finish adds their terms
 
   uint32_t lds_s;  // LDS byte address of `lds`, wave-uniform (scalar): DMA destinations are formed in SGPRs
 
@@ -624,12 +625,14 @@ struct Engine {
     if (pe > pb) {
       const uint32_t pm = positive_mask(pairs, pb, pe, own0, (j0 + j) * 32, FWD, lmask(), lane);
       if (pm) {
+        if (apply_pos) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (pm & (1u << q)) {
-            if (FWD) posz += z[q];
-            c[q] -= 1.f;
-          }
+          for (int q = 0; q < 16; ++q)
+            if (pm & (1u << q)) {
+              if (FWD) posz += z[q];
+              c[q] -= 1.f;
+            }
+        }
         if (MET) {
           uint32_t gt = 0u;
 #pragma unroll
@@ -1214,6 +1217,7 @@ struct RowsArgs {
   float* dhpart;   // [units][RW][D]
   float2* rowpart; // [units][RW]
   int4* metpart;   // [units][RW]: Cut Metrics counts (predicted positive, true positive, positives)
+  bool pos_apply;  // positives enter the tiles (c - 1, the loss's sum of their logits); false: counted only
   float* topv;     // [units][RW][KT]: per-split top-KT logits (scoring)
   int32_t* topi;   // [units][RW][KT]: their item ids
 };
@@ -1266,6 +1270,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     en.nX = a.V;
     en.bptr = a.bptr;
     en.pairs = a.pairs;
+    en.apply_pos = a.pos_apply;
   }
 
   for (int idx = slot; idx < cnt; idx += P / 8) {
@@ -1551,9 +1556,10 @@ static int persistent_grid(int per_cu) {
 }
 
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT = 0>
-static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st) {
+static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st, bool pos_apply = true) {
   using G = Geo<T, D, NW, WITH_DH>;
   RowsArgs a;
+  a.pos_apply = pos_apply;
   a.Hc = ws + L.off_Hc;
   a.E = E;
   a.Evp = ws + L.off_Evp;
@@ -1670,14 +1676,18 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
   } while (0)
 
 template <typename T, int D, int NW>
-static hipError_t rows_any(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
+static hipError_t rows_any(const Layout& L, char* ws, const void* E, bool with_dh, bool met, bool pos_apply,
+                           hipStream_t st) {
   if (met)
-    return with_dh ? rows_launch<T, D, NW, true, true>(L, ws, E, st) : rows_launch<T, D, NW, false, true>(L, ws, E, st);
-  return with_dh ? rows_launch<T, D, NW, true, false>(L, ws, E, st) : rows_launch<T, D, NW, false, false>(L, ws, E, st);
+    return with_dh ? rows_launch<T, D, NW, true, true>(L, ws, E, st, pos_apply)
+                   : rows_launch<T, D, NW, false, true>(L, ws, E, st, pos_apply);
+  return with_dh ? rows_launch<T, D, NW, true, false>(L, ws, E, st, pos_apply)
+                 : rows_launch<T, D, NW, false, false>(L, ws, E, st, pos_apply);
 }
 
-hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, hipStream_t st) {
-  CUTBCE_DISPATCH(L.dtype, rows_any, L, ws, E, with_dh, met, st);
+hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with_dh, bool met, bool pos_apply,
+                             hipStream_t st) {
+  CUTBCE_DISPATCH(L.dtype, rows_any, L, ws, E, with_dh, met, pos_apply, st);
 }
 
 template <typename T, int D, int NW>
