@@ -12,13 +12,6 @@ using namespace cutbce;
 
 namespace {
 
-#ifndef CUTBCE_GATHER_POSITIVES
-#define CUTBCE_GATHER_POSITIVES 1
-#endif
-// Where the forward takes its positives (the sparse target correction of the loss and of dH): gathered per row
-// by the finishing kernel (1), or bucketed and folded into the sweep's tiles (0; always so with Cut Metrics).
-constexpr bool kGatherPositives = CUTBCE_GATHER_POSITIVES != 0;
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

@@ -110,6 +110,14 @@ struct Layout {
   size_t total;
 };
 
+#ifndef CUTBCE_GATHER_POSITIVES
+#define CUTBCE_GATHER_POSITIVES 1
+#endif
+// Where the forward takes its positives (the sparse target correction of the loss and of dH): gathered per row
+// by the finishing kernel (1), or bucketed and folded into the sweep's tiles (0). With Cut Metrics the buckets
+// are built either way (the counts need each positive's logit), and with 1 the sweep only counts them.
+constexpr bool kGatherPositives = CUTBCE_GATHER_POSITIVES != 0;
+
 constexpr int kEBlkItems = 256;   // items per block of the E preparation kernel (column-sum granularity)
 constexpr int kScanBlock = 8192;  // elements per block of the multi-block scan
 

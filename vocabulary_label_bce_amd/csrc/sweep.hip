@@ -891,7 +891,9 @@ struct EpiPoly {
 // ---------------------------------------------------------------------------------------------------------
 // F16G: the gradient GEMM runs on f16 operands (G and the slot-packed rows, which the H preparation stores as
 // f16 scaled by a power of two); used by the dE sweep, whose tiles can then take the polynomial epilogue.
-template <int D, bool FWD, bool GRAD, bool F16G = false>
+// POS: the sweep takes positives from the buckets (the dE sweep; the forward only when its positives are not
+// gathered by the finish). Without them the bucket pointers are never read.
+template <int D, bool FWD, bool GRAD, bool F16G = false, bool POS = !FWD || !kGatherPositives>
 struct Pipe {
   static constexpr int NW = 8, KS = D / 16, NDB = D / 32;
   using GOp = typename std::conditional<F16G, f16x8, bf16x8>::type;  // operands of the gradient GEMM
@@ -986,7 +988,7 @@ struct Pipe {
   // the unit's end j1 read as 0 and are never used). A block is loaded 64 steps before it is needed, so no
   // register waits for the load.
   __device__ inline void bkt_dma(int b) const {
-    if (wave < 2) {
+    if (POS && wave < 2) {
       const int64_t first = (int64_t)j0 + 64 * b + 64 * wave;
       const int64_t cnt = (int64_t)j1 + 1 - first;
       const __amdgpu_buffer_rsrc_t r = rsrc((const char*)(bptr + bbase + first), cnt * 4);
@@ -997,8 +999,12 @@ struct Pipe {
   __device__ inline const int* bkt(int b) const { return (const int*)(lds + BKT) + (b & 1) * 128; }
   // At iteration 64b (a barrier iteration, after the barrier): block b is current and the load window moves.
   __device__ inline void block_start(int b) {
-    const int* k = bkt(b);
-    nem = __builtin_amdgcn_ballot_w64(k[lane] != k[lane + 1]);
+    if (POS) {
+      const int* k = bkt(b);
+      nem = __builtin_amdgcn_ballot_w64(k[lane] != k[lane + 1]);
+    } else {
+      nem = 0;
+    }
     window(b);
   }
 
@@ -1124,7 +1130,7 @@ struct Pipe {
         ES::all(zc, c, st);
     }
     if constexpr (POLY) {
-      if (__builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
+      if (POS && __builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
       g[0] = gn[0];
       g[1] = gn[1];
       zc = zn;
@@ -1138,7 +1144,7 @@ struct Pipe {
       }
       e_acc += st.e_inc;
     }
-    if (__builtin_expect((nem >> (i & 63)) & 1, 0)) positives(i, zc, c, posz);
+    if (POS && __builtin_expect((nem >> (i & 63)) & 1, 0)) positives(i, zc, c, posz);
     zc = zn;
   }
 
