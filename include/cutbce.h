@@ -21,7 +21,7 @@
  *   - Pointers marked (device) must point to device memory of the GPU that is current on the calling thread;
  *     pointers marked (host) to host memory. The caller owns and allocates all memory; the library never
  *     allocates device memory and keeps no state between calls (apart from the opt-in timing records of
- *     cutbce_profile_enable).
+ *     cutbce_profile_enable and the fixed per-GPU scratch array of cutbce_forward_noalloc).
  *   - H [R][D], E [V][D], dH [R][D], dE [V][D] are dense row-major, in the problem's element type, 16-byte
  *     aligned. row_offsets int32 [R+1] (row_offsets[0] = 0, non-decreasing, row_offsets[R] <= nnz); item_ids
  *     int32 [nnz], any order within a row, repeats allowed, entries from row_offsets[R] on unused (so a
@@ -36,8 +36,8 @@
  *     item_ids; cutbce_validate_targets reports them on the device.
  *   - Results are deterministic: the same inputs on the same device give bitwise identical outputs (no
  *     floating-point atomics).
- *   - The workspace is scratch: its contents on entry are ignored and on return are unspecified. Concurrent
- *     calls must use distinct workspaces.
+ *   - The workspace (device, cutbce_workspace_size() bytes, 256-byte aligned) is scratch: its contents on
+ *     entry are ignored and on return are unspecified. Concurrent calls must use distinct workspaces.
  *   - The first compute call of a problem type on a device also sets up per-kernel launch data (dynamic LDS
  *     limit, resident workgroups per CU). Later calls enqueue kernel launches only (no memset or memcpy), so a
  *     caller can capture them into a HIP graph and replay it; the replays read the inputs anew.
@@ -57,7 +57,8 @@ typedef enum {
     CUTBCE_ERR_NULL = 1,        /* a required pointer is NULL */
     CUTBCE_ERR_SHAPE = 2,       /* R < 1, V < 1, nnz < 0, or sizes overflow the supported range */
     CUTBCE_ERR_DTYPE = 3,       /* unknown element type */
-    CUTBCE_ERR_ALIGN = 4,       /* H, E, dH, dE, workspace not 16-byte aligned, or int / float arrays not 4-byte */
+    CUTBCE_ERR_ALIGN = 4,       /* H, E, dH, dE, dh_saved not 16-byte aligned, the workspace not 256-byte
+                                 * aligned, or int / float arrays not 4-byte aligned */
     CUTBCE_ERR_WORKSPACE = 5,   /* workspace smaller than cutbce_workspace_size() */
     CUTBCE_ERR_UNSUPPORTED = 6, /* (dtype, D) combination without a kernel: see cutbce_problem */
     CUTBCE_ERR_HIP = 7          /* a HIP launch or runtime call failed */
@@ -69,7 +70,8 @@ typedef enum {
 } cutbce_dtype;
 
 /* Problem description (host struct). Supported: bf16 with D in {64, 128, 256, 512}; f32 with D in
- * {64, 128, 256}. R, V < 2^31 - 256; nnz < 2^31. */
+ * {64, 128, 256}. 1 <= R, V <= 2^31 - 1025 (the library pads both to a multiple of 256 and keeps 32-bit
+ * indices); 0 <= nnz <= 2^31 - 1. */
 typedef struct {
     int64_t rows;  /* R = B*N positions (Section III-A flattens batch and sequence) */
     int64_t vocab; /* V items */
@@ -138,7 +140,7 @@ cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void
 cutbce_status cutbce_validate_targets(const cutbce_problem *p, const int32_t *row_offsets,
                                       const int32_t *item_ids, int32_t *bad, void *stream);
 
-/* Full-vocabulary top-k scoring (the evaluation of Section I-E: hidden states projected onto every item, items
+/* Full-vocabulary top-k scoring (the evaluation of Section III-E: hidden states projected onto every item, items
  * ranked, Hit@k). For each valid row r, the k items with the largest logits z_rv = H[r] . E[v], ranked by logit
  * (descending) and, among equal logits, by item id (ascending); the logits are never written to memory.
  *   k          1 <= k <= 8 and k <= V.
@@ -173,6 +175,16 @@ cutbce_status cutbce_targets_to_csr(int64_t rows, int32_t slots, const int32_t *
  * recorded (later ones are not timed). Not thread-safe. */
 cutbce_status cutbce_profile_enable(int on);
 cutbce_status cutbce_profile_read(double *ms, int64_t *launches, int n_kinds);
+
+/* MFMA-only ceiling of the device (a measurement, not part of the loss): launches `blocks` workgroups of
+ * `waves_per_block` waves (1..16), each wave running `iters` rounds of four independent
+ * v_mfma_f32_32x32x16_bf16 -- the sweeps' instruction -- on register operands, with no memory traffic.
+ * One round is 4 * 32768 flops. Lane 0 of wave w writes stamps[4w .. 4w+3] = (s_memtime before, after,
+ * s_memrealtime before, after): shader-clock ticks and 100 MHz reference ticks, so the clock the device held is
+ * 0.1 GHz * (t1 - t0) / (r1 - r0).
+ *   stamps (device) int64 [4 * blocks * waves_per_block], 8-byte aligned.
+ * Errors: SHAPE for counts out of range, NULL, ALIGN. Asynchronous on `stream`. */
+cutbce_status cutbce_mfma_ceiling(int blocks, int waves_per_block, int iters, long long *stamps, void *stream);
 
 /* Static description of a status code (host). */
 const char *cutbce_status_string(cutbce_status s);

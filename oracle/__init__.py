@@ -6,7 +6,7 @@ It shares no code with the GPU library (``vocabulary_label_bce_amd``) and never 
 The arithmetic lives in ``cutbce_oracle.c`` (plain C, float64, OpenMP over rows/items); this module only
 compiles it with gcc and marshals arrays. See the header of the C file for the equations it follows
 ("Cut Binary Cross Entropy", Section III-A Eq. (1)-(3), Section III-B Eq. (4), the Cut Metrics of
-Section III-D and the full-vocabulary top-k / Hit@k evaluation of Section I-E).
+Section III-D and the full-vocabulary top-k / Hit@k evaluation of Section III-E).
 """
 from __future__ import annotations
 

@@ -30,7 +30,7 @@
  *   - W = 0 (every row masked, or all weights 0) gives loss 0 and zero gradients;
  *   - row_loss[r] is the unnormalised, unweighted sum_v L(z_rv, y_rv) of a valid row and 0 for a masked row.
  *
- * Full-vocabulary top-k (Section I-E evaluation): per valid row, the k items with the largest logits, ordered
+ * Full-vocabulary top-k (Section III-E evaluation): per valid row, the k items with the largest logits, ordered
  * by logit (descending) and, among equal logits, by item id (ascending); Hit@k counts a row as a hit when at
  * least one of its positives is among them.
  *
@@ -362,7 +362,7 @@ int oracle_metrics(int64_t R, int64_t V, int D, int dtype, const void *H, const 
             mark_row(row_offsets, item_ids, r, ymap, 1);
             for (int64_t v = 0; v < V; ++v) {
                 double z = dot_rv(H, E, dtype, r, v, D);
-#if ORACLE_PLANT == 6
+#if ORACLE_PLANT == 8
                 int pred = z >= 0.0; /* planted: a zero logit predicted positive */
 #else
                 int pred = z > 0.0;
@@ -383,7 +383,7 @@ int oracle_metrics(int64_t R, int64_t V, int D, int dtype, const void *H, const 
 
 /* Does (za, va) rank before (zb, vb): larger logit first, smaller item id among equal logits. */
 static int ranks_before(double za, int64_t va, double zb, int64_t vb) {
-#if ORACLE_PLANT == 7
+#if ORACLE_PLANT == 9
     return za > zb || (za == zb && va > vb); /* planted: ties broken towards the larger id */
 #else
     return za > zb || (za == zb && va < vb);

@@ -87,6 +87,21 @@ def test_forward_rejects_bad_arguments():
                          weight=FAKE + 2) == 4  # misaligned row weights
     # nnz > 0 needs item_ids
     assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=0, mask=FAKE, loss=FAKE, ws=FAKE) == 1
+    # the workspace must be 256-byte aligned (16 is not enough)
+    assert _call_forward(good, H=FAKE, E=FAKE, ro=FAKE, ids=FAKE, mask=FAKE, loss=FAKE, ws=FAKE + 128) == 4
+
+
+def test_size_limits_at_their_boundaries():
+    """R and V up to 2^31 - 1025 are accepted (the workspace size is computed), one more is SHAPE; nnz up to
+    2^31 - 1."""
+    lim = (1 << 31) - 1025
+    sz = ctypes.c_size_t()
+    lib = B.lib()
+    for R, V, nnz in [(lim, 4096, 100), (64, lim, 100), (64, 4096, (1 << 31) - 1)]:
+        assert lib.cutbce_workspace_size(ctypes.byref(B.Problem(R, V, nnz, 64, 1)), ctypes.byref(sz)) == 0
+        assert sz.value > 0
+    for R, V, nnz in [(lim + 1, 4096, 100), (64, lim + 1, 100), (64, 4096, 1 << 31)]:
+        assert lib.cutbce_workspace_size(ctypes.byref(B.Problem(R, V, nnz, 64, 1)), ctypes.byref(sz)) == 2
 
 
 def test_backward_and_validate_reject_bad_arguments():
@@ -174,6 +189,15 @@ def test_product_modules_never_import_the_oracle():
             elif isinstance(node, ast.ImportFrom):
                 mods = [node.module or ""]
             assert not any(m == "oracle" or m.startswith("oracle.") for m in mods), (name, mods)
+
+
+def test_mfma_ceiling_rejects_bad_arguments():
+    L = B.lib()
+    assert L.cutbce_mfma_ceiling(0, 8, 10, 8, None) == 2       # no workgroups
+    assert L.cutbce_mfma_ceiling(1, 17, 10, 8, None) == 2      # more than 16 waves
+    assert L.cutbce_mfma_ceiling(1, 8, 0, 8, None) == 2        # no iterations
+    assert L.cutbce_mfma_ceiling(1, 8, 10, None, None) == 1    # no stamp buffer
+    assert L.cutbce_mfma_ceiling(1, 8, 10, 12, None) == 4      # misaligned stamp buffer
 
 
 def test_noalloc_forward_rejects_problems_beyond_its_scratch_before_any_hip_call():

@@ -1,4 +1,4 @@
-"""GPU full-vocabulary top-k and Hit@k ("Cut Binary Cross Entropy", Section I-E evaluation) through the C ABI,
+"""GPU full-vocabulary top-k and Hit@k ("Cut Binary Cross Entropy", Section III-E evaluation) through the C ABI,
 against the float64 oracle.
 
 The GPU ranks float32 logits; two items whose float64 logits differ by less than the float32 dot-product error
@@ -74,6 +74,25 @@ def test_topk_matches_oracle(name, kw, k):
     vals, ids, hits = topk(d["H"], d["E"], k, d["row_offsets"], d["item_ids"], d["row_mask"])
     torch.cuda.synchronize()
     _check(p, k, vals.cpu().numpy(), ids.cpu().numpy(), hits.cpu().numpy())
+
+
+@pytest.mark.parametrize("V,D", [(257, 128), (300, 64), (511, 512)])
+def test_topk_never_returns_padding_items(V, D):
+    """V % 256 in (0, 256): the sweep runs up to 7 whole padding steps past V (and a ragged one). Every real
+    logit is made negative (H >= 0, E <= 0), so a padding item (logit 0) would outrank all of them if it
+    slipped through."""
+    p = W.custom_problem(64, V, D, dtype="bf16", seed=59, h_std=0.5, e_std=0.5, pos_per_row=(1, 4),
+                         mask_frac=0.1)
+    p["H"] = p["H"].abs() + 0.01
+    p["E"] = -(p["E"].abs() + 0.01)
+    d = {key: v.cuda() for key, v in p.items()}
+    vals, ids, hits = topk(d["H"], d["E"], 8, d["row_offsets"], d["item_ids"], d["row_mask"])
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    m = p["row_mask"].numpy() == 1
+    assert (got[m] >= 0).all() and (got[m] < V).all()
+    assert (vals.cpu().numpy()[m] < 0).all()
+    _check(p, 8, vals.cpu().numpy(), got, hits.cpu().numpy())
 
 
 def test_topk_ties_pick_smaller_ids():

@@ -104,6 +104,27 @@ def test_near_zero_count_and_row_subset():
     assert (sub == allr[[4, 0, 7]]).all()
 
 
+def test_near_zero_count_at_intermediate_eps():
+    """Logits fixed exactly by construction (H[r] = (1, 0), E[v] = (a_v, 0), so z = a_v, powers of two): the count
+    of |z| <= eps follows the list, with eps inclusive at a logit's magnitude."""
+    a = np.array([0.5, -0.25, 2.0 ** -7, -(2.0 ** -6), 2.0 ** -5, 0.0625, 0.0, -(2.0 ** -9)], np.float32)
+    V = a.size
+    H = torch.tensor([[1.0, 0.0], [2.0, 0.0]])
+    E = torch.zeros(V, 2)
+    E[:, 0] = torch.from_numpy(a)
+    ro = torch.tensor([0, 2, 3], dtype=torch.int32)
+    ids = torch.tensor([2, 4, 0], dtype=torch.int32)
+    m = torch.ones(2, dtype=torch.uint8)
+    for eps, want0 in [(0.03, 4), (2.0 ** -5, 5), (2.0 ** -8, 2), (0.3, 7)]:
+        got = oracle.metrics(H, E, ro, ids, m, eps=eps)
+        assert got[0, 4] == want0, (eps, got[0])
+        # row 1 has logits 2 a: its count is that of row 0 at eps / 2
+        assert got[1, 4] == oracle.metrics(H[:1], E, ro[:2], ids, m[:1], eps=eps / 2)[0, 4]
+    # predictions: z > 0 for 0.5, 2^-7, 2^-5, 0.0625; positives of row 0 are items 2 and 4 (both predicted)
+    got = oracle.metrics(H, E, ro, ids, m, eps=0.0)
+    assert list(got[0, :4]) == [2, 2, 0, 4]
+
+
 def test_planted_tie_rule_is_caught():
-    """6: a zero logit predicted positive."""
-    assert pin_brute_force(plant=6) > 0 or pin_zero_E(plant=6) > 0
+    """8: a zero logit predicted positive."""
+    assert pin_brute_force(plant=8) > 0 or pin_zero_E(plant=8) > 0

@@ -1,4 +1,4 @@
-"""Pins for the oracle's full-vocabulary top-k and Hit@k ("Cut Binary Cross Entropy", Section I-E: the
+"""Pins for the oracle's full-vocabulary top-k and Hit@k ("Cut Binary Cross Entropy", Section III-E: the
 evaluation projects hidden states to full-vocabulary logits, ranks the items, and counts a user as a hit when
 one of the held-out items is among the top 8). Ranking: larger logit first, smaller item id among equal logits.
 
@@ -88,5 +88,5 @@ def test_row_subset_and_hits_on_planted_positive():
 
 
 def test_planted_tie_break_is_caught():
-    """7: ties broken towards the larger item id."""
-    assert pin_brute_force(plant=7) > 0 or pin_ties(plant=7) > 0
+    """9: ties broken towards the larger item id."""
+    assert pin_brute_force(plant=9) > 0 or pin_ties(plant=9) > 0

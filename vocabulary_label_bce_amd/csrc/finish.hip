@@ -213,7 +213,7 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
   return hipGetLastError();
 }
 
-// Scoring finish (full-vocabulary top-k, the evaluation of "Cut Binary Cross Entropy" Section I-E): one wave
+// Scoring finish (full-vocabulary top-k, the evaluation of "Cut Binary Cross Entropy" Section III-E): one wave
 // per row merges the S per-split top-KT lists of the forward sweep into the row's k best items -- larger
 // logit first, smaller item id among equal logits -- by k rounds of a wave-wide selection over candidates held
 // in registers, and counts how many of them are positives of the row (Hit@k: the row is a hit when the count is

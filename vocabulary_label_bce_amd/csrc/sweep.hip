@@ -20,7 +20,7 @@
 // no registers) into two rings, one for the d-packed operand of the logit GEMM and one for the slot-packed
 // operand of the gradient GEMM; workgroup barriers come every few steps (see Geo).
 //
-// The forward sweep also serves full-vocabulary scoring (top-k per row, Section I-E's evaluation) with a
+// The forward sweep also serves full-vocabulary scoring (top-k per row, Section III-E's evaluation) with a
 // running top list per lane in place of the loss epilogue, and can count the Cut Metrics of Section III-D.
 #include <atomic>
 #include <type_traits>
@@ -592,10 +592,11 @@ struct Engine {
   __device__ inline void epilogue(int j, int pb, int pe, const f32x16& z, GP& g, float& e_acc, float& posz,
                                   int* met, TopK<KT ? KT : 1>* tk) {
     if constexpr (KT > 0) {
-      // scoring: keep the lane's best items (real items only; the last step may hold padding). Only the values
-      // above the lane's current k-th best are inserted, one at a time, picked by a select chain (no dynamic
-      // register indexing). Items past the vocabulary exist only in its last step: the lane's bound (32-bit,
-      // V < 2^31) is all-pass elsewhere.
+      // scoring: keep the lane's best items (real items only: V is padded to a multiple of 256, so up to 7
+      // whole steps past V are swept, besides a ragged last one). Only the values above the lane's current k-th
+      // best are inserted, one at a time, picked by a select chain (no dynamic register indexing). The lane's
+      // bound lim (32-bit, V < 2^31) is 32 for steps wholly below V, the number of real items left in a step
+      // holding V, and <= 0 -- nothing passes -- for steps at or beyond V.
       const float thr = tk->last();
       const int item0 = (j0 + j) * 32 + (lane / 32) * 4;
       const int lim = (int64_t)(j0 + j + 1) * 32 > nX ? (int)nX - item0 : 32;  // items of this lane below V
