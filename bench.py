@@ -157,6 +157,29 @@ def bench_topk(a, cfg, prob, R_v):
     }))
 
 
+def mfma_ceiling(torch, B, dev):
+    """MFMA-only ceiling (cutbce_mfma_ceiling): one workgroup of 8 waves per CU (two per SIMD, as in the D = 128
+    sweeps), each issuing v_mfma_f32_32x32x16_bf16 back to back from registers. Returns its rate and the shader
+    clock the device held meanwhile (s_memtime over s_memrealtime ticks, median over waves)."""
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    waves, iters = 8, 50000
+    stamps = torch.zeros(4 * blocks * waves, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.mfma_ceiling(blocks, waves, iters, stamps, stream)  # warm-up launch
+    ev0.record(stream)
+    B.mfma_ceiling(blocks, waves, iters, stamps, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    st = stamps.view(-1, 4).double()
+    ghz = (0.1 * (st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).median().item()
+    tflops = blocks * waves * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    return {"kernel": "k_mfma_ceiling (v_mfma_f32_32x32x16_bf16 from registers, 8 waves per CU)",
+            "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "clock_ghz": round(ghz, 3), "ms": round(ms, 3), "iters": iters, "blocks": blocks, "waves": waves}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -182,6 +205,9 @@ def main():
     V, D = E.shape
     if a.topk:
         return bench_topk(a, cfg, prob, R_v)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    mem_base, free0 = torch.cuda.memory_allocated(dev), torch.cuda.mem_get_info(dev)[0]
     w = Workspace(H, E, ids, want_row_loss=False, save_dh=True, want_metrics=a.metrics)
     g = torch.ones(1, dtype=torch.float32, device=dev)
 
@@ -193,6 +219,12 @@ def main():
         step()
     torch.cuda.synchronize()
     loss0 = float(w.loss.item())
+    # device memory of the calls: the caching allocator's peak and the drop of free memory since before the
+    # workspace and outputs were allocated, against a dense [rows, V] float32 logits buffer
+    memory = {"workspace_bytes": w.ws.numel() * w.ws.element_size(),
+              "allocator_peak_bytes": torch.cuda.max_memory_allocated(dev) - mem_base,
+              "device_free_drop_bytes": free0 - torch.cuda.mem_get_info(dev)[0],
+              "dense_logits_fp32_bytes": W.dense_logits_bytes(cfg.R, V)}
     B.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -244,7 +276,12 @@ def main():
                     for k, d in kern.items()},
         "roofline": roof,
         "loss": loss0,
+        "memory": memory,
     }
+    ceil = mfma_ceiling(torch, B, dev)
+    if dom:
+        ceil["dominant_kernel_frac_of_ceiling"] = round(kern[dom]["tflops"] / ceil["tflops"], 4)
+    out["mfma_ceiling"] = ceil
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prob, R_v, a.cpu_seconds)
     if a.copy_mib > 0:

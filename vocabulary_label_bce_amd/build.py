@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcutbce.so")
-SOURCES = ["prep.hip", "sweep.hip", "finish.hip", "api.hip"]
+SOURCES = ["prep.hip", "sweep.hip", "finish.hip", "api.hip", "ceiling.hip"]
 ARCH = os.environ.get("CUTBCE_ARCH", "gfx950")
 
 # Packed-fp32 VALU instructions are disabled for all device code (plain float code is used instead).
