@@ -503,6 +503,27 @@ static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, hipStream_
 //    atomic and the others take the following slots. With many ids per row and hot items, one atomic per id
 //    serialises on the hot buckets' counters.
 // ---------------------------------------------------------------------------------------------------------
+// Wave-aggregated counter increments: the active lanes that target one bucket make a single atomic (issued by
+// the first of them), and each gets base + its rank among them. Many lanes of a wave hit the same bucket when
+// items are hot (a Zipf head in one item tile), where one atomic per id would serialise on that counter.
+// Uniform control flow: every lane of the wave must call it.
+__device__ inline int aggregated_add(int32_t* __restrict__ cnt, int64_t b, bool active) {
+  const int lane = lane_id();
+  uint64_t todo = __ballot(active);
+  int slot = 0;
+  while (todo) {
+    const int leader = __builtin_ctzll(todo);
+    const int64_t bl = __shfl(b, leader, 64);
+    const uint64_t m = __ballot(active && b == bl) & todo;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&cnt[bl], __popcll(m));
+    base = __shfl(base, leader, 64);
+    if ((m >> lane) & 1) slot = base + __popcll(m & ((1ull << lane) - 1));
+    todo &= ~m;
+  }
+  return slot;
+}
+
 template <bool kScatter>
 __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
                                                 const int32_t* __restrict__ ids, int64_t V, bool rows_side,
@@ -510,22 +531,27 @@ __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, con
                                                 int2* __restrict__ pairs, int* bad) {
   const int64_t k = (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8;
   const int sub = threadIdx.x % 8;
-  if (k >= ctl->n_valid) return;
-  const int2 rp = rptr[k];
+  const bool row = k < ctl->n_valid;
+  const int2 rp = row ? rptr[k] : make_int2(0, 0);
+  // the wave's longest row sets the (uniform) number of rounds
+  int len = rp.y - rp.x;
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) len = max(len, __shfl_xor(len, o, 64));
   int nbad = 0;
-  for (int p = rp.x + sub; p < rp.y; p += 8) {
-    const int v = ids[p];
-    if (v < 0 || v >= V) {
-      ++nbad;
-      continue;
+  for (int p0 = 0; p0 < len; p0 += 8) {
+    const int p = rp.x + p0 + sub;
+    bool act = p < rp.y;
+    int v = 0;
+    if (act) {
+      v = ids[p];
+      if (v < 0 || v >= V) {
+        ++nbad;
+        act = false;
+      }
     }
-    const int64_t b = rows_side ? (k / tile) * nsteps_minor + v / 32 : (v / tile) * nsteps_minor + k / 32;
-    if (kScatter) {
-      const int pos = atomicAdd(&cnt[b], 1);
-      pairs[pos] = make_int2((int)k, v);
-    } else {
-      atomicAdd(&cnt[b], 1);
-    }
+    const int64_t b = rows_side ? (k / tile) * nsteps_minor + v / 32 : ((int64_t)v / tile) * nsteps_minor + k / 32;
+    const int pos = aggregated_add(cnt, b, act);
+    if (kScatter && act) pairs[pos] = make_int2((int)k, v);
   }
   if (!kScatter && nbad) atomicAdd(bad, nbad);
 }
