@@ -56,7 +56,8 @@ __device__ inline void gather_positives(const int2* __restrict__ rptr, const int
         keep = keep & (uj != v);
       }
     }
-    for (int j = 0; j < 63; ++j) {  // earlier lanes of this chunk
+    const int nq = rg.y - q0 < 64 ? rg.y - q0 : 64;  // ids in this chunk (uniform)
+    for (int j = 0; j + 1 < nq; ++j) {              // earlier lanes of this chunk
       const int u = __shfl(v, j, 64);
       keep = keep & !(j < lane && u == v);
     }

@@ -227,12 +227,18 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const int32_t* __restrict__ row_of,
                                                 const float* __restrict__ wc, int D, T* __restrict__ Hc,
                                                 T* __restrict__ Hrp, double* __restrict__ sum_part,
-                                                Ctl* __restrict__ stats) {
+                                                Ctl* __restrict__ stats, const Ctl* __restrict__ ctl) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
   __shared__ float wt[32];
   const int tid = threadIdx.x;
   const int64_t k0 = (int64_t)blockIdx.x * 32;
+  // no sweep reads compacted rows at or past the valid rows rounded up to a 256-row tile: such blocks only zero
+  // their column-sum partials
+  if (k0 >= (((int64_t)ctl->n_valid + 255) / 256) * 256) {
+    for (int d = tid; d < D; d += 256) sum_part[blockIdx.x * (int64_t)D + d] = 0.0;
+    return;
+  }
   if (tid < 32) wt[tid] = wc[k0 + tid];
   // gather rows (16-byte units)
   const int upr = D * (int)sizeof(T) / 16;  // 16-byte units per row
@@ -294,6 +300,7 @@ __global__ void __launch_bounds__(256) k_prep_hrp16(const __bf16* __restrict__ H
                                                     const Ctl* __restrict__ ctl, int D, _Float16* __restrict__ Hrp) {
   const int tid = threadIdx.x;
   const int64_t k0 = (int64_t)blockIdx.x * 32;
+  if (k0 >= (((int64_t)ctl->n_valid + 255) / 256) * 256) return;  // rows no sweep reads (see k_prep_h)
   const int sh = hrp_shift(ctl->hw_absmax);
   const int runs = (D / 32) * 2 * 64;
   _Float16* dst = Hrp + k0 * D;
@@ -348,12 +355,13 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
     hipLaunchKernelGGL(k_prep_h<__bf16>, dim3((unsigned)nblk), dim3(256), sm, st, (const __bf16*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
                        (__bf16*)(ws + L.off_Hc), want_hrp && !f16rp ? (__bf16*)(ws + L.off_Hrp) : nullptr,
-                       (double*)(ws + L.off_sumH_part), f16rp ? ctl : nullptr);
+                       (double*)(ws + L.off_sumH_part), f16rp ? ctl : nullptr, (const Ctl*)ctl);
   } else {
     hipLaunchKernelGGL(k_prep_h<float>, dim3((unsigned)nblk), dim3(256), sm, st, (const float*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
                        (float*)(ws + L.off_Hc),
-                       want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part), nullptr);
+                       want_hrp ? (float*)(ws + L.off_Hrp) : nullptr, (double*)(ws + L.off_sumH_part), nullptr,
+                       (const Ctl*)ctl);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
