@@ -37,7 +37,8 @@
  *   - Results are deterministic: the same inputs on the same device give bitwise identical outputs (no
  *     floating-point atomics).
  *   - The workspace (device, cutbce_workspace_size() bytes, 256-byte aligned) is scratch: its contents on
- *     entry are ignored and on return are unspecified. Concurrent calls must use distinct workspaces.
+ *     entry are ignored (except by cutbce_backward_reuse, which reads what cutbce_forward left) and on return
+ *     are unspecified. Concurrent calls must use distinct workspaces.
  *   - The first compute call of a problem type on a device also sets up per-kernel launch data (dynamic LDS
  *     limit, resident workgroups per CU). Later calls enqueue kernel launches only (no memset or memcpy), so a
  *     caller can capture them into a HIP graph and replay it; the replays read the inputs anew.
@@ -132,6 +133,20 @@ cutbce_status cutbce_backward(const cutbce_problem *p, const void *H, const void
                               const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
                               const float *row_weight, const float *grad_loss, const float *dh_saved, void *dH,
                               void *dE, void *workspace, size_t workspace_bytes, void *stream);
+
+/* cutbce_backward after the cutbce_forward it belongs to, on the same workspace: the backward of a training step
+ * (Section III-B's custom VJP), reusing the row compaction (valid rows, their weights and id ranges, s) and the H
+ * preparation (compacted rows, column sums, row norms) that cutbce_forward left in the workspace instead of
+ * recomputing them. Arguments, outputs and errors as for cutbce_backward, and the results are the same bits.
+ * Precondition (not checkable without a host synchronisation): the last call on `workspace` was cutbce_forward
+ * with the same problem, H, row_offsets, item_ids, row_mask and row_weight, none of which has changed since (E is
+ * not part of what is reused; the forward need not have been given dh_saved). If the precondition
+ * does not hold the gradients are wrong, but every read stays inside the arrays and every loop ends: the kernels
+ * clamp the valid-row count to R and the id ranges to [0, nnz]. */
+cutbce_status cutbce_backward_reuse(const cutbce_problem *p, const void *H, const void *E,
+                                    const int32_t *row_offsets, const int32_t *item_ids, const uint8_t *row_mask,
+                                    const float *row_weight, const float *grad_loss, const float *dh_saved,
+                                    void *dH, void *dE, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device-side check of the targets: writes to *bad (device int32) the number of ids outside [0, V) plus
  * the number of rows whose offsets decrease, plus 1 if row_offsets[0] != 0 or row_offsets[R] > nnz (ids are

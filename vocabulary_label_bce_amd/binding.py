@@ -31,7 +31,7 @@ class Problem(ctypes.Structure):
 
 
 EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_forward_noalloc", "cutbce_backward",
-           "cutbce_validate_targets",
+           "cutbce_backward_reuse", "cutbce_validate_targets",
            "cutbce_targets_to_csr", "cutbce_topk",
            "cutbce_profile_enable", "cutbce_profile_read", "cutbce_mfma_ceiling", "cutbce_status_string",
            "cutbce_version"]
@@ -52,6 +52,7 @@ def lib():
         L.cutbce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cutbce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.cutbce_backward_reuse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.cutbce_validate_targets.argtypes = [P, vp, vp, vp, vp]
         L.cutbce_targets_to_csr.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_int32, vp, vp, vp]
         L.cutbce_topk.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
@@ -65,7 +66,7 @@ def lib():
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
         for f in ("cutbce_workspace_size", "cutbce_forward", "cutbce_forward_noalloc", "cutbce_backward",
-                  "cutbce_validate_targets",
+                  "cutbce_backward_reuse", "cutbce_validate_targets",
                   "cutbce_targets_to_csr", "cutbce_topk"):
             getattr(L, f).restype = i32
         _lib = L
@@ -129,11 +130,13 @@ def forward_noalloc(p: Problem, H, E, row_offsets, item_ids, row_mask, loss, row
 
 
 def backward(p: Problem, H, E, row_offsets, item_ids, row_mask, grad_loss, dh_saved, dH, dE, ws, stream=None,
-             row_weight=None):
-    """cutbce_backward on device tensors (dH / dE overwritten in place; either may be None)."""
-    _check(lib().cutbce_backward(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids),
-                                 _ptr(row_mask), _ptr(row_weight), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH),
-                                 _ptr(dE), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+             row_weight=None, reuse=False):
+    """cutbce_backward on device tensors (dH / dE overwritten in place; either may be None). reuse=True calls
+    cutbce_backward_reuse: `ws` must hold what cutbce_forward left for these same inputs."""
+    f = lib().cutbce_backward_reuse if reuse else lib().cutbce_backward
+    _check(f(ctypes.byref(p), _ptr(H), _ptr(E), _ptr(row_offsets), _ptr(item_ids), _ptr(row_mask),
+             _ptr(row_weight), _ptr(grad_loss), _ptr(dh_saved), _ptr(dH), _ptr(dE), _ptr(ws),
+             ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def topk(p: Problem, H, E, row_offsets, item_ids, row_mask, k: int, top_vals, top_ids, hits, ws, stream=None):

@@ -257,10 +257,11 @@ cutbce_status cutbce_forward_noalloc(const cutbce_problem* p, const void* H, con
                         (size_t)CUTBCE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
-cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
-                              const int32_t* item_ids, const uint8_t* row_mask, const float* row_weight,
-                              const float* grad_loss, const float* dh_saved, void* dH, void* dE, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// reuse: the workspace holds the row compaction and H preparation of a cutbce_forward on the same inputs
+static cutbce_status backward_impl(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
+                                   const int32_t* item_ids, const uint8_t* row_mask, const float* row_weight,
+                                   const float* grad_loss, const float* dh_saved, void* dH, void* dE, void* workspace,
+                                   size_t workspace_bytes, void* stream, bool reuse) {
   Layout L;
   cutbce_status s = check_common(p, H, E, row_offsets, item_ids, row_mask, workspace, workspace_bytes, &L);
   if (s != CUTBCE_OK) return s;
@@ -271,8 +272,12 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (!dH && !dE) return CUTBCE_OK;
-  TRY(launch_compact(L, ws, row_mask, row_weight, row_offsets, st));
-  TRY(launch_prep_h(L, ws, H, dE != nullptr, st));
+  if (!reuse) {
+    TRY(launch_compact(L, ws, row_mask, row_weight, row_offsets, st));
+    TRY(launch_prep_h(L, ws, H, dE != nullptr, st));
+  } else if (dE) {
+    TRY(launch_prep_hrp(L, ws, H, st));
+  }
   if (dE) {
     TRY(launch_buckets(L, ws, item_ids, false, st));
     TRY(timed_items(L, ws, E, grad_loss, dE, st));
@@ -291,6 +296,22 @@ cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void
     }
   }
   return CUTBCE_OK;
+}
+
+cutbce_status cutbce_backward(const cutbce_problem* p, const void* H, const void* E, const int32_t* row_offsets,
+                              const int32_t* item_ids, const uint8_t* row_mask, const float* row_weight,
+                              const float* grad_loss, const float* dh_saved, void* dH, void* dE, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return backward_impl(p, H, E, row_offsets, item_ids, row_mask, row_weight, grad_loss, dh_saved, dH, dE, workspace,
+                       workspace_bytes, stream, false);
+}
+
+cutbce_status cutbce_backward_reuse(const cutbce_problem* p, const void* H, const void* E,
+                                    const int32_t* row_offsets, const int32_t* item_ids, const uint8_t* row_mask,
+                                    const float* row_weight, const float* grad_loss, const float* dh_saved, void* dH,
+                                    void* dE, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(p, H, E, row_offsets, item_ids, row_mask, row_weight, grad_loss, dh_saved, dH, dE, workspace,
+                       workspace_bytes, stream, true);
 }
 
 cutbce_status cutbce_validate_targets(const cutbce_problem* p, const int32_t* row_offsets, const int32_t* item_ids,

@@ -132,6 +132,9 @@ __host__ __device__ constexpr inline int sweep_waves(int dtype, int D) {
 hipError_t launch_compact(const Layout& L, char* ws, const uint8_t* mask, const float* weight,
                           const int32_t* row_offsets, hipStream_t st);
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st);
+// The dE sweep's slot-packed rows Hrp from a workspace whose row compaction and H preparation are done (bf16: the
+// f16 copy from Hc and the row statistics; f32: the H preparation again, with Hrp).
+hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t st);
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st);
 hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bool rows_side, hipStream_t st);
 // pos_apply: the positives of the buckets enter the tiles (c - 1 and the sum of their logits); false: with Cut

@@ -287,9 +287,16 @@ __global__ void __launch_bounds__(256) k_prep_h(const T* __restrict__ H, const i
       nr = fmaxf(nr, __shfl_xor(nr, o, 64));
       am = fmaxf(am, __shfl_xor(am, o, 64));
     }
+    // the block's maxima, then one atomic per field and block
+    __shared__ float sh_nr[4], sh_am[4];
     if (lane_id() == 0) {
-      atomicMax(&stats->hnorm_max, __float_as_uint(nr));
-      atomicMax(&stats->hw_absmax, __float_as_uint(am));
+      sh_nr[tid / 64] = nr;
+      sh_am[tid / 64] = am;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      atomicMax(&stats->hnorm_max, __float_as_uint(fmaxf(fmaxf(sh_nr[0], sh_nr[1]), fmaxf(sh_nr[2], sh_nr[3]))));
+      atomicMax(&stats->hw_absmax, __float_as_uint(fmaxf(fmaxf(sh_am[0], sh_am[1]), fmaxf(sh_am[2], sh_am[3]))));
     }
   }
 }
@@ -352,10 +359,11 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   const bool f16rp = want_hrp && hrp_is_f16(L.dtype, L.D);
   Ctl* ctl = (Ctl*)(ws + L.off_ctl);
   if (L.dtype == 1) {
+    // bf16 always takes the row statistics, so that a backward can reuse this preparation (launch_prep_hrp)
     hipLaunchKernelGGL(k_prep_h<__bf16>, dim3((unsigned)nblk), dim3(256), sm, st, (const __bf16*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
                        (__bf16*)(ws + L.off_Hc), want_hrp && !f16rp ? (__bf16*)(ws + L.off_Hrp) : nullptr,
-                       (double*)(ws + L.off_sumH_part), f16rp ? ctl : nullptr, (const Ctl*)ctl);
+                       (double*)(ws + L.off_sumH_part), ctl, (const Ctl*)ctl);
   } else {
     hipLaunchKernelGGL(k_prep_h<float>, dim3((unsigned)nblk), dim3(256), sm, st, (const float*)H,
                        (const int32_t*)(ws + L.off_row_of), (const float*)(ws + L.off_wc), L.D,
@@ -365,13 +373,16 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (f16rp) {
-    hipLaunchKernelGGL(k_prep_hrp16, dim3((unsigned)nblk), dim3(256), 0, st, (const __bf16*)(ws + L.off_Hc),
-                       (const float*)(ws + L.off_wc), (const Ctl*)ctl, L.D, (_Float16*)(ws + L.off_Hrp));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if (f16rp && (e = launch_prep_hrp(L, ws, H, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
                      (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t st) {
+  if (!hrp_is_f16(L.dtype, L.D)) return launch_prep_h(L, ws, H, true, st);  // f32: the copy comes from H
+  hipLaunchKernelGGL(k_prep_hrp16, dim3((unsigned)(L.R_pad / 32)), dim3(256), 0, st, (const __bf16*)(ws + L.off_Hc),
+                     (const float*)(ws + L.off_wc), (const Ctl*)(ws + L.off_ctl), L.D, (_Float16*)(ws + L.off_Hrp));
   return hipGetLastError();
 }
 
@@ -532,15 +543,23 @@ __device__ inline int aggregated_add(int32_t* __restrict__ cnt, int64_t b, bool 
   return slot;
 }
 
+// A compacted row's id range [x, y) clamped into [0, nnz] (the compaction already clamps it; clamping again keeps
+// the reads inside item_ids whatever the workspace holds).
+__device__ inline int2 clamp_range(int2 r, int64_t nnz) {
+  const int n = (int)nnz;
+  const int b = min(max(r.x, 0), n);
+  return make_int2(b, min(max(r.y, b), n));
+}
+
 template <bool kScatter>
 __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
-                                                const int32_t* __restrict__ ids, int64_t V, bool rows_side,
-                                                int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
-                                                int2* __restrict__ pairs, int* bad) {
+                                                const int32_t* __restrict__ ids, int64_t V, int64_t nnz,
+                                                bool rows_side, int tile, int64_t nsteps_minor,
+                                                int32_t* __restrict__ cnt, int2* __restrict__ pairs, int* bad) {
   const int64_t k = (int64_t)blockIdx.x * (blockDim.x / 8) + threadIdx.x / 8;
   const int sub = threadIdx.x % 8;
   const bool row = k < ctl->n_valid;
-  const int2 rp = row ? rptr[k] : make_int2(0, 0);
+  const int2 rp = row ? clamp_range(rptr[k], nnz) : make_int2(0, 0);
   // the wave's longest row sets the (uniform) number of rounds
   int len = rp.y - rp.x;
 #pragma unroll
@@ -566,13 +585,13 @@ __global__ void __launch_bounds__(256) k_bucket(const Ctl* __restrict__ ctl, con
 
 template <bool kScatter>
 __global__ void __launch_bounds__(256) k_bucket_runs(const Ctl* __restrict__ ctl, const int2* __restrict__ rptr,
-                                                     const int32_t* __restrict__ ids, int64_t V, bool rows_side,
-                                                     int tile, int64_t nsteps_minor, int32_t* __restrict__ cnt,
-                                                     int2* __restrict__ pairs, int* bad) {
+                                                     const int32_t* __restrict__ ids, int64_t V, int64_t nnz,
+                                                     bool rows_side, int tile, int64_t nsteps_minor,
+                                                     int32_t* __restrict__ cnt, int2* __restrict__ pairs, int* bad) {
   const int64_t k = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // one row per wave
   const int lane = lane_id();
   if (k >= ctl->n_valid) return;  // the whole wave
-  const int2 rp = rptr[k];
+  const int2 rp = clamp_range(rptr[k], nnz);
   int nbad = 0;
   for (int p0 = rp.x; p0 < rp.y; p0 += 64) {  // uniform across the wave
     const int p = p0 + lane;
@@ -621,7 +640,7 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
   const int64_t blocks = runs ? L.R_pad / 4 : L.R_pad / 32;  // rows per 256-thread block: 4 or 32
   if (L.nnz > 0) {
     hipLaunchKernelGGL(runs ? k_bucket_runs<false> : k_bucket<false>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bptr,
+                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, L.nnz, rows_side, tile, minor, bptr,
                        (int2*)nullptr, &ctl->bad_ids);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -632,7 +651,7 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
     hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cblocks), dim3(256), 0, st, bfill, (const int32_t*)bptr, nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(runs ? k_bucket_runs<true> : k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, rows_side, tile, minor, bfill, pairs,
+                       ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, L.nnz, rows_side, tile, minor, bfill, pairs,
                        (int*)nullptr);
   }
   return hipGetLastError();

@@ -1412,7 +1412,8 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
 #pragma unroll
   for (int db = 0; db < NDBE; ++db) acc[db] = f32x16{};
 
-  const int n_valid = a.ctl->n_valid;
+  // clamped to the padded rows, so that no workspace contents can make the sweep run past them
+  const int n_valid = min(max(a.ctl->n_valid, 0), (int)a.R_pad);
   const int n_st = (n_valid + 31) / 32;
   constexpr bool kPipe = use_pipe<T, D, NW, false, 0, DEPART>();
   if (kPipe && n_st > 0) {

@@ -51,6 +51,9 @@ class _CutBCE(torch.autograd.Function):
         B.forward(p, H, E, row_offsets, item_ids, row_mask, loss, None, dh_saved, ws, row_weight=row_weight)
         ctx.save_for_backward(H, E, row_offsets, item_ids, row_mask, dh_saved, row_weight)
         ctx.p = p
+        # the workspace keeps the forward's row preparation for the backward (cutbce_backward_reuse); autograd's
+        # version check on the saved inputs rejects an in-place change of them in between
+        ctx.ws = ws if (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]) else None
         return loss[0]
 
     @staticmethod
@@ -60,9 +63,10 @@ class _CutBCE(torch.autograd.Function):
         g = g.reshape(1).to(dtype=torch.float32).contiguous()
         dH = torch.empty_like(H) if ctx.needs_input_grad[0] else None
         dE = torch.empty_like(E) if ctx.needs_input_grad[1] else None
-        if dH is not None or dE is not None:
-            ws = B.alloc_workspace(p, H.device)
-            B.backward(p, H, E, row_offsets, item_ids, row_mask, g, dh_saved, dH, dE, ws, row_weight=row_weight)
+        ws, ctx.ws = ctx.ws, None
+        if (dH is not None or dE is not None) and ws is not None:
+            B.backward(p, H, E, row_offsets, item_ids, row_mask, g, dh_saved, dH, dE, ws, row_weight=row_weight,
+                       reuse=True)
         return dH, dE, None, None, None, None
 
 
@@ -163,9 +167,11 @@ class Workspace:
         return self.loss
 
     def backward(self, H, E, row_offsets, item_ids, row_mask, grad=None, want_dH=True, want_dE=True,
-                 use_saved=True, stream=None, row_weight=None):
+                 use_saved=True, stream=None, row_weight=None, reuse=False):
+        """reuse=True: the previous call on this workspace was forward() with the same H, targets, mask and
+        weights (cutbce_backward_reuse skips the row compaction and the H preparation)."""
         g = self.grad if grad is None else grad
         B.backward(self.p, H, E, row_offsets, item_ids, row_mask, g, self.dh_saved if use_saved else None,
                    self.dH if want_dH else None, self.dE if want_dE else None, self.ws, stream,
-                   row_weight=row_weight)
+                   row_weight=row_weight, reuse=reuse)
         return (self.dH if want_dH else None), (self.dE if want_dE else None)
