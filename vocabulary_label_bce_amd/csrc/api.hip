@@ -42,9 +42,8 @@ Layout make_layout(const cutbce_problem* p) {
   L.esz = p->dtype == CUTBCE_BF16 ? 2 : 4;
   L.R_pad = round_up(L.R, kPad);
   L.V_pad = round_up(L.V, kPad);
-  const int nw = sweep_waves(L.dtype, L.D);
-  L.rows_per_wg = nw * 32;
-  L.items_per_wg = nw * 32;
+  L.rows_per_wg = sweep_waves(L.dtype, L.D) * 32;
+  L.items_per_wg = items_tile(L.dtype, L.D);
   L.n_rt = L.R_pad / L.rows_per_wg;
   L.n_vt = L.V_pad / L.items_per_wg;
   L.n_rs = L.R_pad / 32;

@@ -81,6 +81,14 @@ struct Ctl {           // device control block
 // keeps 10 fraction bits instead of bf16's 7).
 __host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return dtype == 1 && D > 0; }
 
+// Shapes whose sweeps run on the 16-owner engine (bf16, D = 256 and 512): a wave owns 16 rows or items and the
+// MFMAs are 16x16x32 tiles (lane l supplies A[m = l%16][k = 8(l/16) + j] and B[k = 8(l/16) + j][n = l%16], j < 8,
+// and holds D[m = 4(l/16) + i][n = l%16], i < 4). Its slot-packed copies (Evp, Hrp) of a 32-row block X use:
+// for 16-wide d-block db and lane l, the 8 elements X[sp16_row(l, j)][16 db + l % 16] (j = 0..7) stored together.
+__host__ __device__ constexpr inline bool narrow_owner(int dtype, int D) { return dtype == 1 && D >= 256; }
+__host__ __device__ constexpr inline int sp16_row(int lane, int j) { return 16 * (j / 4) + 4 * (lane / 16) + (j % 4); }
+__host__ __device__ constexpr inline int64_t sp16_off(int db, int lane) { return ((int64_t)db * 64 + lane) * 8; }
+
 // Power of two that brings the largest |w_r H[r][d]| into [2^14, 2^15) (0 when every value is 0), so that the f16
 // copy keeps 11 significant bits for every value within 2^29 of the largest.
 __device__ inline int hrp_shift(uint32_t absmax_bits) {
@@ -121,9 +129,18 @@ constexpr bool kGatherPositives = CUTBCE_GATHER_POSITIVES != 0;
 constexpr int kEBlkItems = 256;   // items per block of the E preparation kernel (column-sum granularity)
 constexpr int kScanBlock = 8192;  // elements per block of the multi-block scan
 
-// Launch configuration of the two sweeps for a (dtype, D): waves per workgroup.
+// Waves per workgroup of the 32-owner sweeps for a (dtype, D); a workgroup's row tile (and, except for the
+// 16-owner dE sweep, item tile) is 32 of these. bf16 D = 512: only the scoring sweep runs on it, with the row tiles
+// of the 16-owner forward (64 rows).
 __host__ __device__ constexpr inline int sweep_waves(int dtype, int D) {
-  return (dtype == 1) ? (D <= 128 ? 8 : 4) : (D <= 64 ? 8 : 4);
+  return (dtype == 1) ? (D <= 128 ? 8 : (D == 256 ? 4 : 2)) : (D <= 64 ? 8 : 4);
+}
+// Waves per workgroup of the 16-owner forward (bf16, D >= 256): two per SIMD at D = 256; one at D = 512, where
+// the owner operand and the dH accumulators take 192 registers and two waves would spill.
+__host__ __device__ constexpr inline int rows16_waves(int D) { return D == 512 ? 4 : 8; }
+// Item tile of the dE sweep: 8 waves x 16 items on the 16-owner engine, else 32 per wave.
+__host__ __device__ constexpr inline int items_tile(int dtype, int D) {
+  return narrow_owner(dtype, D) ? 128 : sweep_waves(dtype, D) * 32;
 }
 
 // ---------------------------------------------------------------------------------------------------------

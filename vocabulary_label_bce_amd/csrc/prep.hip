@@ -309,8 +309,22 @@ __global__ void __launch_bounds__(256) k_prep_hrp16(const __bf16* __restrict__ H
   const int64_t k0 = (int64_t)blockIdx.x * 32;
   if (k0 >= (((int64_t)ctl->n_valid + 255) / 256) * 256) return;  // rows no sweep reads (see k_prep_h)
   const int sh = hrp_shift(ctl->hw_absmax);
-  const int runs = (D / 32) * 2 * 64;
   _Float16* dst = Hrp + k0 * D;
+  if (narrow_owner(1, D)) {
+    // the 16-owner engine's layout (D >= 256)
+    for (int q = tid; q < (D / 16) * 64; q += 256) {
+      const int lane = q % 64, db = q / 64;
+      f16x8 run;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = sp16_row(lane, j);
+        run[j] = (_Float16)ldexpf((float)Hc[(k0 + row) * D + db * 16 + lane % 16] * wc[k0 + row], sh);
+      }
+      *(f16x8*)(dst + sp16_off(db, lane)) = run;
+    }
+    return;
+  }
+  const int runs = (D / 32) * 2 * 64;
   for (int q = tid; q < runs; q += 256) {
     const int lane = q % 64, g = (q / 64) % 2, db = q / 128;
     f16x8 run;
@@ -408,7 +422,22 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
       *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = x;
     }
     __syncthreads();
-    if (Evp) {
+    bool packed = false;
+    if constexpr (sizeof(T) == 2) {
+      if (Evp && narrow_owner(1, D)) {
+        // the 16-owner engine's layout (bf16, D >= 256)
+        T* dst = Evp + v0 * D;
+        for (int q = tid; q < (D / 16) * 64; q += 256) {
+          const int lane = q % 64, db = q / 64;
+          bf16x8 run;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) run[j] = tile[sp16_row(lane, j) * D + db * 16 + lane % 16];
+          *(bf16x8*)(dst + sp16_off(db, lane)) = run;
+        }
+        packed = true;
+      }
+    }
+    if (Evp && !packed) {
       T* dst = Evp + v0 * D;
       const int runs = (D / 32) * Elem<T>::kGroups * 64;
       for (int q = tid; q < runs; q += 256) {

@@ -242,12 +242,13 @@ __device__ inline typename Elem<T>::Op lds_b(const char* blk, int db, int g, int
 //   softplus(z) - z - ln 2 = [|z|/2 + ln((1 + e^-|z|) / 2)] - z/2,   c = sign(z) (1/(1 + e^-|z|) - 1/2).
 constexpr float kFastProd = 0x1p120f;
 
-// c_i = 1/w_i - 1/2 for 16 factors w_i >= 1 with pair products w2 and quad products w4 (each below 2^126):
+// c_i = 1/w_i - 1/2 for 4Q factors w_i >= 1 (16 by default) with pair products w2 and quad products w4 (each below 2^126):
 // one reciprocal per quad, then down the product tree (batch inversion): 1/(w0 w1) = w2 w3 / (w0 w1 w2 w3),
 // 1/w0 = w1 / (w0 w1), ...; each 1/w_i picks up two extra roundings.
+template <int Q = 4>
 __device__ inline void inv_minus_half(const float* w, const float* w2, const float* w4, float* c) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const float r4 = __builtin_amdgcn_rcpf(w4[q]);
     const float ra = r4 * w2[2 * q + 1], rb = r4 * w2[2 * q];
     c[4 * q] = ra * w[4 * q + 1] - 0.5f;
@@ -1512,6 +1513,507 @@ __global__ void __launch_bounds__(256) k_items_tail(ItemsArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// The 16-owner engine (bf16, D = 256 and 512). A wave owns 16 rows (forward) or 16 items (dE) and streams 32
+// per step through the rings of Engine, on 16x16x32 MFMA tiles: the owner operand (D / 32 registers of 8 values)
+// and the gradient accumulators (D / 16 tiles of 4 registers) fit two waves per SIMD even at D = 512, where a
+// 32-owner wave needs twice as many and runs alone on its SIMD (the forward then in two passes). Each MFMA takes
+// one 16-byte LDS read, as the 32x32x16 engines do for twice the work; the epilogue has 8 values per lane and
+// step against 2 * D / 16 MFMAs.
+//
+// Logit tile of step j, half h (streamed 16h..16h+15): A = streamed rows from the d-packed block, B = owner
+// operand, so lane l holds z[h][i] of owner l % 16 and streamed 16h + 4(l/16) + i. Its 8 values, in the order
+// 4h + i, are the lane's k-slots 8(l/16) .. 8(l/16) + 7 of the gradient GEMM: A = G (owner l % 16), B = the
+// slot-packed block (sp16_row gives each slot's streamed row), acc[db] holds owner 4(l/16) + i, d = 16 db + l % 16.
+// ---------------------------------------------------------------------------------------------------------
+
+// Forward epilogue on 8 logits of one lane (the 16-value form of epi_rows with one quad pair fewer).
+template <bool GRAD, bool LOSS>
+__device__ inline void epi_rows8(const float* z, float* c, float& e_acc) {
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 1.f + __builtin_amdgcn_exp2f(z[i] * -kLog2e);
+  float w2[4], w4[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w2[i] = w[2 * i] * w[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) w4[i] = w2[2 * i] * w2[2 * i + 1];
+  const float wp = w4[0] * w4[1];
+  if (GRAD) inv_minus_half<2>(w, w2, w4, c);
+  float e_inc = LOSS ? kLn2 * (__builtin_amdgcn_logf(wp) - 8.f) : 0.f;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(wp <= kFastProd)) != 0, 0)) {
+    float u[8], wa[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u[i] = __builtin_fabsf(z[i]) * -kLog2e;
+      wa[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
+    }
+    float a2[4], a4[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a2[i] = wa[2 * i] * wa[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a4[i] = a2[2 * i] * a2[2 * i + 1];
+    if (GRAD) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float r4 = __builtin_amdgcn_rcpf(a4[q]);
+        const float ra = r4 * a2[2 * q + 1], rb = r4 * a2[2 * q];
+        const float r[4] = {ra * wa[4 * q + 1], ra * wa[4 * q], rb * wa[4 * q + 3], rb * wa[4 * q + 2]};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(r[k] - 0.5f, z[4 * q + k]);
+      }
+    }
+    if (LOSS) {
+      float us = 0.f, zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        us += u[i];
+        zs += z[i];
+      }
+      e_inc = kLn2 * (__builtin_amdgcn_logf(a4[0] * a4[1]) - 8.f - 0.5f * us) - 0.5f * zs;
+    }
+  }
+  if (LOSS) e_acc += e_inc;
+}
+
+// dE epilogue on 8 logits: c = 1/(1 + e^-z) - 1/2.
+__device__ inline void epi_items8(const float* z, float* c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z[i] * -kLog2e)) - 0.5f;
+}
+
+// Per-lane positive mask of a 16-owner step: bit 4h + i of lane o + 16 q is the pair (owner o, streamed
+// 16h + 4q + i). Same bucket walk as positive_mask.
+__device__ inline uint32_t positive_mask16(const int2* __restrict__ pairs, int pb, int pe, int own, int stream0,
+                                           bool owner_is_row, uint32_t* lmask, int lane) {
+  lmask[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int q0 = pb; q0 < pe; q0 += 64) {
+    const int q = q0 + lane;
+    if (q < pe) {
+      const int2 kv = pairs[q];
+      const int o = (owner_is_row ? kv.x : kv.y) - own;
+      const int sidx = (owner_is_row ? kv.y : kv.x) - stream0;
+      if (o >= 0 && o < 16 && sidx >= 0 && sidx < 32)
+        atomicOr(&lmask[o + 16 * ((sidx >> 2) & 3)], 1u << (4 * (sidx >> 4) + (sidx & 3)));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  return lmask[lane];
+}
+
+// The 8-value epilogues of epi_rows8 / epi_items8 cut into stages, so that the 16-owner engine can place them
+// between the MFMAs of an iteration (same operations, same order of rounding; the forward's |z| form runs in
+// finish(), after the MFMAs, and only when a lane's product passes kFastProd).
+template <bool FWD, bool GRAD>
+struct Epi8 {
+  static constexpr int NS = FWD ? (GRAD ? 6 : 4) : 5;  // stages
+  float z[8], t[8], c[8], w2[4], w4[2], r4[2], lg;
+  __device__ inline void stage(int st) {
+    if (st == 0 || st == 1) {
+#pragma unroll
+      for (int i = 4 * st; i < 4 * st + 4; ++i)
+        t[i] = FWD ? 1.f + __builtin_amdgcn_exp2f(z[i] * -kLog2e) : __builtin_amdgcn_exp2f(z[i] * -kLog2e);
+      return;
+    }
+    if constexpr (FWD) {
+      if (st == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w2[i] = t[2 * i] * t[2 * i + 1];
+        w4[0] = w2[0] * w2[1];
+        w4[1] = w2[2] * w2[3];
+      } else if (st == 3) {
+        lg = __builtin_amdgcn_logf(w4[0] * w4[1]);
+        if (GRAD) {
+          r4[0] = __builtin_amdgcn_rcpf(w4[0]);
+          r4[1] = __builtin_amdgcn_rcpf(w4[1]);
+        }
+      } else if (GRAD && (st == 4 || st == 5)) {
+        const int q = st - 4;  // inv_minus_half for quad q
+        const float ra = r4[q] * w2[2 * q + 1], rb = r4[q] * w2[2 * q];
+        c[4 * q] = ra * t[4 * q + 1] - 0.5f;
+        c[4 * q + 1] = ra * t[4 * q] - 0.5f;
+        c[4 * q + 2] = rb * t[4 * q + 3] - 0.5f;
+        c[4 * q + 3] = rb * t[4 * q + 2] - 0.5f;
+      }
+    } else {
+      if (st == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = 1.f + t[i];
+      } else if (st == 3 || st == 4) {
+#pragma unroll
+        for (int i = 4 * (st - 3); i < 4 * (st - 3) + 4; ++i) c[i] = __builtin_amdgcn_rcpf(t[i]) - 0.5f;
+      }
+    }
+  }
+  // Runs the stages in one go (an iteration that deals none out).
+  __device__ inline void all_stages() {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) stage(st);
+  }
+  // forward: the loss term (or the |z| form of loss and c for a tile whose product passes kFastProd)
+  __device__ inline void finish(float& e_acc) {
+    if constexpr (FWD) {
+      const float wp = w4[0] * w4[1];
+      float e_inc = kLn2 * (lg - 8.f);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(wp <= kFastProd)) != 0, 0)) {
+        float u[8], wa[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u[i] = __builtin_fabsf(z[i]) * -kLog2e;
+          wa[i] = 1.f + __builtin_amdgcn_exp2f(u[i]);
+        }
+        float a2[4], a4[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a2[i] = wa[2 * i] * wa[2 * i + 1];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a4[i] = a2[2 * i] * a2[2 * i + 1];
+        if (GRAD) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float rr = __builtin_amdgcn_rcpf(a4[q]);
+            const float ra = rr * a2[2 * q + 1], rb = rr * a2[2 * q];
+            const float x[4] = {ra * wa[4 * q + 1], ra * wa[4 * q], rb * wa[4 * q + 3], rb * wa[4 * q + 2]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[4 * q + k] = __builtin_copysignf(x[k] - 0.5f, z[4 * q + k]);
+          }
+        }
+        float us = 0.f, zs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          us += u[i];
+          zs += z[i];
+        }
+        e_inc = kLn2 * (__builtin_amdgcn_logf(a4[0] * a4[1]) - 8.f - 0.5f * us) - 0.5f * zs;
+      }
+      e_acc += e_inc;
+    }
+  }
+};
+
+template <int D, bool FWD, bool GRAD, bool MET, int NW = 8, bool POS = !FWD || MET || !kGatherPositives>
+struct Eng16 {
+  static constexpr int KB = D / 32, NDB = D / 16;
+  // One wave per SIMD (NW = 4): the epilogue's stages are dealt out between the MFMAs and the whole order is
+  // pinned, since no other wave fills the vector ALU; two waves per SIMD (NW = 8): the compiler places the
+  // vector work between the pinned MFMAs and LDS reads.
+  static constexpr bool kStaged = NW == 4;
+  using R = Engine<__bf16, D, NW, FWD, GRAD, MET>;  // rings, their loads and barriers, bucket pointers
+  using G = Geo<__bf16, D, NW, GRAD>;
+  using GOp = typename std::conditional<FWD, bf16x8, f16x8>::type;  // dE: f16 G and f16 slot-packed rows
+  struct Z {
+    f32x4 h[2];
+  };
+  R r;
+  bool apply_pos = true;
+  __device__ inline void setup(char* l, int w, int ln) { r.setup(l, w, ln); }
+
+  // The A ring holds each step's block operand-major: the 1 KB at (2 kb + h) * 1024 is the A operand of k-block
+  // kb, half h, lane l's 16 bytes at l * 16 (streamed row 16h + l%16, features 32 kb + 8 (l/16) .. + 7). The DMA
+  // writes 16 bytes per lane at consecutive LDS addresses from a per-lane global offset, so the permutation costs
+  // nothing there, and every operand read is conflict-free at one lane address plus a constant.
+  __device__ inline void dma_a(int rel, int slot) const {
+    const int64_t row0 = (int64_t)r.clampj(rel) * 32;
+    const char* xa = (const char*)r.X + row0 * (int64_t)(D * 2);
+    const int64_t rem = (r.nX - row0) * (int64_t)(D * 2);
+    const int nrec = rem <= 0 ? 0 : (rem > (int64_t)G::kStepBytes ? G::kStepBytes : (int)rem);
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)xa, (short)0, nrec, 0x00020000);
+    const uint32_t dst = r.lds_s + slot * G::kStepBytes;
+    static_assert(G::kLoadB == 16 && G::kWaveBytes == 1024, "one 1 KB operand per wave instruction");
+#pragma unroll
+    for (int q = 0; q < G::kLoadsPerPart; ++q) {
+      const int inst = r.wave + q * NW;  // operand (kb, h) = (inst / 2, inst % 2)
+      const int voff = (16 * (inst % 2) + r.lane % 16) * (D * 2) + (32 * (inst / 2) + 8 * (r.lane / 16)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(size_t)(dst + inst * 1024), 16, voff, 0, 0, 0);
+    }
+  }
+  // Start of iteration i: the barrier (every kK iterations, with the bucket refill) and the iteration's loads.
+  __device__ inline void top(int i) {
+    if (G::kK == 1 || i % G::kK == 0) {
+      if (POS)
+        r.barrier_at(i);
+      else
+        wait_vm_and_barrier<G::kInFlight>();
+    }
+    dma_a(i + G::kLA, (i + G::kLA) % G::kNA);
+    if (GRAD) r.dma_b(i + G::kLB);
+  }
+  using EP = Epi8<FWD, GRAD>;
+  // End of step j's epilogue, after its stages: loss, positives of the step (bucket [pb, pe)), Cut Metrics counts,
+  // the G tile.
+  __device__ inline void epilogue_end(int j, int pb, int pe, EP& es, GOp& g, float& posz, int* met) {
+    uint32_t gt = 0u;  // bit q: z[q] > 0 (Cut Metrics)
+    if (MET) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) gt |= (es.z[q] > 0.f ? 1u : 0u) << q;
+      met[0] += __builtin_popcount(gt);
+    }
+    if (POS && pe > pb) {
+      const uint32_t pm = positive_mask16(r.pairs, pb, pe, r.own0, (r.j0 + j) * 32, FWD, r.lmask(), r.lane);
+      if (pm) {
+        if (apply_pos) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (pm & (1u << q)) {
+              if (FWD) posz += es.z[q];
+              if (GRAD) es.c[q] -= 1.f;
+            }
+        }
+        if (MET) {
+          met[1] += __builtin_popcount(pm & gt);
+          met[2] += __builtin_popcount(pm);
+        }
+      }
+    }
+    if (GRAD) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) g[q] = (typename std::conditional<FWD, __bf16, _Float16>::type)es.c[q];
+    }
+  }
+  // Iteration i: ring loads and barrier, logits of step i + 1 (into zn; NEXT), gradient GEMM of step i - 1 (PREV),
+  // epilogue of step i (zc). MFMA order: per k-block, logit half 0, gradient d-block 2kb, logit half 1, gradient
+  // d-block 2kb + 1 (a logit chain's MFMAs four apart). Each MFMA's LDS operand is read three MFMAs ahead into a
+  // ring of four registers, and the epilogue's stages are dealt out between the MFMAs; the whole order is pinned
+  // (sched_barrier): the compiler would otherwise either hoist every read of the iteration or, short of
+  // registers, wait for each read right before its MFMA, and it left the forward's epilogue after the MFMAs. The
+  // first and last iterations are peeled, so the main loop has no conditions.
+  // The pinned MFMA sequence: logits into zn from the A slot of step ia (kL), gradient GEMM into acc from the B
+  // slot of step ig (kG).
+  template <bool kL, bool kG, bool kE = false>
+  __device__ inline void mfma_seq(int ia, int ig, const bf16x8* own, Z& zn, const GOp& g, f32x4* acc,
+                                  EP* es = nullptr) const {
+    constexpr int NM = (kL ? 2 * KB : 0) + (kG ? NDB : 0);
+    constexpr int PER = kE ? (NM / EP::NS > 0 ? NM / EP::NS : 1) : 1;  // MFMAs per epilogue stage
+    const char* pa = r.lds + (ia % G::kNA) * G::kStepBytes + r.lane * 16;
+    const char* pg = r.lds + (G::kNA + ig % (G::kNB ? G::kNB : 1)) * G::kStepBytes + r.lane * 16;
+    if (kL) {
+      zn.h[0] = f32x4{};
+      zn.h[1] = f32x4{};
+    }
+    // MFMA k: logit (k-block, half) or gradient (d-block)
+    auto is_l = [](int k) { return kL && (!kG || (k & 1) == 0); };
+    auto l_kb = [](int k) { return kG ? k / 4 : k / 2; };
+    auto l_h = [](int k) { return kG ? (k / 2) & 1 : k & 1; };
+    auto g_db = [](int k) { return kL ? 2 * (k / 4) + ((k / 2) & 1) : k; };
+    auto read = [&](int k) -> u32x4 {
+      return is_l(k) ? *(const u32x4*)(pa + (2 * l_kb(k) + l_h(k)) * 1024) : *(const u32x4*)(pg + g_db(k) * 1024);
+    };
+    constexpr int RB = NW == 4 ? 6 : 4;  // operand ring: reads RB - 1 MFMAs ahead
+    u32x4 buf[RB];
+#pragma unroll
+    for (int k = 0; k < RB - 1; ++k)
+      if (k < NM) buf[k] = read(k);
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+      if (k + RB - 1 < NM) buf[(k + RB - 1) % RB] = read(k + RB - 1);
+      const u32x4 op = buf[k % RB];
+      if (is_l(k)) {
+        const int h = l_h(k);
+        zn.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), own[l_kb(k)], zn.h[h],
+                                                          0, 0, 0);
+      } else if constexpr (FWD) {
+        acc[g_db(k)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g, __builtin_bit_cast(bf16x8, op), acc[g_db(k)], 0, 0,
+                                                               0);
+      } else {
+        acc[g_db(k)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(g, __builtin_bit_cast(f16x8, op), acc[g_db(k)], 0, 0,
+                                                              0);
+      }
+      if (kE && k % PER == PER - 1 && k / PER < EP::NS) es->stage(k / PER);
+      __builtin_amdgcn_sched_barrier(kStaged ? 0 : 0x0406);  // unstaged: VALU, SALU, transcendentals may cross
+    }
+    if (kE && NM / PER < EP::NS) {  // stages left over (a sequence shorter than the epilogue)
+#pragma unroll
+      for (int st = NM / PER; st < EP::NS; ++st) es->stage(st);
+    }
+  }
+  template <bool NEXT, bool PREV>
+  __device__ inline void iter(int i, const bf16x8* own, const Z& zc, Z& zn, GOp& g, f32x4* acc, float& e_acc,
+                              float& posz, int* met) {
+    __builtin_amdgcn_sched_barrier(0);
+    top(i);
+    int pb = 0, pe = 0;
+    if (POS) r.bkt_get(i, pb, pe);
+    EP es;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) es.z[q] = zc.h[q / 4][q % 4];
+    if (kStaged) {
+      mfma_seq<NEXT, GRAD && PREV, true>(i + 1, i - 1, own, zn, g, acc, &es);
+    } else {
+      mfma_seq<NEXT, GRAD && PREV, false>(i + 1, i - 1, own, zn, g, acc);
+      es.all_stages();
+    }
+    es.finish(e_acc);
+    epilogue_end(i, pb, pe, es, g, posz, met);
+  }
+  __device__ inline void run(const bf16x8* own, f32x4* acc, float& e_acc, float& posz, int* met) {
+    const int n = r.j1 - r.j0;
+    if (n <= 0) return;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // everyone is done with the previous unit's rings
+#pragma unroll
+    for (int q = 0; q < G::kLA; ++q) dma_a(q, q % G::kNA);
+    if (GRAD) {
+#pragma unroll
+      for (int q = 0; q < G::kLB; ++q) r.dma_b(q);
+    }
+    if (POS) r.bkt_init();
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    GOp g;
+    Z zc, zn;
+    mfma_seq<true, false>(0, 0, own, zc, g, acc);  // step 0
+    if (n == 1) {
+      iter<false, false>(0, own, zc, zn, g, acc, e_acc, posz, met);
+    } else {
+      iter<true, false>(0, own, zc, zn, g, acc, e_acc, posz, met);
+      for (int i = 1; i < n - 1; ++i) {
+        zc = zn;  // eight moves per 2 * D / 16 MFMAs
+        iter<true, true>(i, own, zc, zn, g, acc, e_acc, posz, met);
+      }
+      zc = zn;
+      iter<false, true>(n - 1, own, zc, zn, g, acc, e_acc, posz, met);
+    }
+    wait_vm_and_barrier<0>();  // the slot-packed block of step n - 1 has landed
+    if (GRAD) mfma_seq<false, true>(0, n - 1, own, zn, g, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+};
+
+// Forward sweep on the 16-owner engine: the unit loop, splits and partial layouts of k_rows (row tiles of NW waves
+// x 16 rows: 128 at D = 256, two waves per SIMD; 64 at D = 512, one wave per SIMD).
+template <int D, bool WITH_DH, bool MET, int NW>
+__global__ void __launch_bounds__(NW * 64) k_rows16(RowsArgs a) {
+  using EN = Eng16<D, true, WITH_DH, MET, NW>;
+  constexpr int RW = NW * 16, KB = D / 32, NDB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+  const __bf16* __restrict__ Hc = (const __bf16*)a.Hc;
+  const int n_valid = a.ctl->n_valid;
+  const int Tt = (n_valid + RW - 1) / RW;
+  if (Tt == 0) return;
+  const int n_steps = (int)(a.V_pad / 32);
+  const int P = gridDim.x;
+  const int S = choose_splits(Tt, n_steps, P);
+  if (blockIdx.x == 0 && tid == 0) a.ctl->splits = S;
+  const int U = Tt * S;
+  const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int start = (int)(((int64_t)x * U) / 8), cnt = (int)(((int64_t)(x + 1) * U) / 8) - start;
+  EN en;
+  en.setup(lds, wave, lane);
+  en.r.X = (const __bf16*)a.E;
+  en.r.Xsp = (const __bf16*)a.Evp;
+  en.r.nX = a.V;
+  en.r.bptr = a.bptr;
+  en.r.pairs = a.pairs;
+  en.apply_pos = a.pos_apply;
+  for (int idx = slot; idx < cnt; idx += P / 8) {
+    const int u = start + idx;
+    const int s = u / Tt, t = u % Tt;
+    const int r_base = t * RW + wave * 16;
+    en.r.j0 = (int)(((int64_t)s * n_steps) / S);
+    en.r.j1 = (int)(((int64_t)(s + 1) * n_steps) / S);
+    en.r.bbase = (int64_t)t * a.n_vs;
+    en.r.own0 = r_base;
+    // lane addresses made opaque, so that the compiler does not hoist per-offset partial addresses out of the
+    // unit loop (they would stay live across it)
+    const __bf16* hp = Hc + (int64_t)(r_base + lane % 16) * D + (lane / 16) * 8;
+    asm volatile("" : "+v"(hp));
+    bf16x8 hop[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hop[kb] = *(const bf16x8*)(hp + kb * 32);
+    f32x4 acc[WITH_DH ? NDB : 1];
+#pragma unroll
+    for (int db = 0; db < (WITH_DH ? NDB : 1); ++db) acc[db] = f32x4{};
+    float e_acc = 0.f, posz = 0.f;
+    int met[3] = {0, 0, 0};
+    en.run(hop, acc, e_acc, posz, met);
+    // lanes o, o + 16, o + 32, o + 48 hold row o's sums
+    const int64_t urow = (int64_t)u * RW + wave * 16;
+    float e_tot = e_acc + __shfl_xor(e_acc, 16, 64), p_tot = posz + __shfl_xor(posz, 16, 64);
+    e_tot += __shfl_xor(e_tot, 32, 64);
+    p_tot += __shfl_xor(p_tot, 32, 64);
+    if (lane < 16) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    if (MET) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        met[q] += __shfl_xor(met[q], 16, 64);
+        met[q] += __shfl_xor(met[q], 32, 64);
+      }
+      if (lane < 16) a.metpart[urow + lane] = make_int4(met[0], met[1], met[2], 0);
+    }
+    if (WITH_DH) {
+      float* dp = a.dhpart + (urow + 4 * (lane / 16)) * D + lane % 16;
+      asm volatile("" : "+v"(dp));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[i * D + db * 16] = acc[db][i];
+    }
+  }
+}
+
+// dE sweep on the 16-owner engine: item tiles of 8 waves x 16 items = 128, halved tail tiles as in k_items.
+template <int D>
+__global__ void __launch_bounds__(512) k_items16(ItemsArgs a) {
+  using EN = Eng16<D, false, true, false>;
+  constexpr int IW = 128, KB = D / 32, NDB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+  const __bf16* __restrict__ E = (const __bf16*)a.E;
+  const int b = blockIdx.x;
+  const int split = b >= a.n_full ? (b - a.n_full) / 2 : -1;
+  const int part = b >= a.n_full ? (b - a.n_full) % 2 : 0;
+  const int t = split < 0 ? b : a.n_full + split;
+  const int64_t v_own0 = (int64_t)t * IW + wave * 16;  // first item of this wave
+  const int64_t v_mine = v_own0 + lane % 16;
+  bf16x8 eop[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    eop[kb] = v_mine < a.V ? *(const bf16x8*)(E + v_mine * D + kb * 32 + (lane / 16) * 8) : bf16x8{};
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
+  const int n_valid = min(max(a.ctl->n_valid, 0), (int)a.R_pad);
+  const int n_st = (n_valid + 31) / 32;
+  if (n_st > 0) {
+    EN en;
+    en.setup(lds, wave, lane);
+    en.r.X = (const __bf16*)a.Hc;
+    en.r.Xsp = (const __bf16*)a.Hrp;  // f16 values; the ring copies bytes
+    en.r.nX = n_valid;
+    en.r.bptr = a.bptr;
+    en.r.pairs = a.pairs;
+    en.r.bbase = (int64_t)t * a.n_rs;
+    en.r.own0 = (int)v_own0;
+    en.r.j0 = split < 0 || part == 0 ? 0 : n_st / 2;
+    en.r.j1 = split < 0 || part == 1 ? n_st : n_st / 2;
+    float e_acc = 0.f, posz = 0.f;
+    en.run(eop, acc, e_acc, posz, nullptr);
+  }
+  if (split >= 0) {
+    float* __restrict__ tp = a.tailpart + ((int64_t)(split * 2 + part) * IW + wave * 16) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tp[(4 * (lane / 16) + i) * D + db * 16 + lane % 16] = acc[db][i];
+    return;
+  }
+  // dE[v][d] = s * g * (acc * 2^-shift + 1/2 sum_r w_r H[r][d])
+  const float scf = (float)(a.ctl->scale * (double)a.grad_loss[0]);
+  const float unscale = ldexpf(1.f, -hrp_shift(a.ctl->hw_absmax));
+  __bf16* __restrict__ dE = (__bf16*)a.dE;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d = db * 16 + lane % 16;
+    const float half = (float)(0.5 * a.sumH[d]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t v = v_own0 + 4 * (lane / 16) + i;
+      if (v < a.V) dE[v * D + d] = (__bf16)(scf * (acc[db][i] * unscale + half));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kMaxDevices = 16;  // devices whose launch data is cached (others query every time)
@@ -1563,8 +2065,48 @@ static int persistent_grid(int per_cu) {
   return P > 0 ? P : 8;
 }
 
+static RowsArgs rows_args(const Layout& L, char* ws, const void* E, bool pos_apply, int KT) {
+  RowsArgs a;
+  a.pos_apply = pos_apply;
+  a.Hc = ws + L.off_Hc;
+  a.E = E;
+  a.Evp = ws + L.off_Evp;
+  a.ctl = (Ctl*)(ws + L.off_ctl);
+  a.bptr = (const int32_t*)(ws + L.off_bptr_r);
+  a.pairs = (const int2*)(ws + L.off_pairs_r);
+  a.V = L.V;
+  a.V_pad = L.V_pad;
+  a.n_vs = L.n_vs;
+  a.R_pad = L.R_pad;
+  a.dhpart = (float*)(ws + L.off_dhpart);
+  a.rowpart = (float2*)(ws + L.off_rowpart);
+  a.metpart = (int4*)(ws + L.off_metpart);
+  a.topv = (float*)(ws + L.off_dhpart);
+  a.topi = (int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * (KT ? KT : 1);
+  return a;
+}
+
+// Forward sweep of bf16 D = 256 / 512 on the 16-owner engine (one pass; the same row tiles of 128 and partials).
+template <int D, bool WITH_DH, bool MET>
+static hipError_t rows_launch16(const Layout& L, char* ws, const void* E, hipStream_t st, bool pos_apply) {
+  constexpr int NW = rows16_waves(D);
+  if (L.rows_per_wg != NW * 16) return hipErrorInvalidValue;  // the layout's row tiles are this kernel's
+  const RowsArgs a = rows_args(L, ws, E, pos_apply, 0);
+  constexpr auto kern = k_rows16<D, WITH_DH, MET, NW>;
+  const size_t sm = Geo<__bf16, D, NW, WITH_DH>::kLdsBytes;
+  int per_cu = 1;
+  hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT = 0>
 static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStream_t st, bool pos_apply = true) {
+  if constexpr (KT == 0 && narrow_owner(sizeof(T) == 2 ? 1 : 0, D)) {
+    static_assert(NW * 32 == rows16_waves(D) * 16, "the scoring engine and the 16-owner engine share row tiles");
+    return rows_launch16<D, WITH_DH, MET>(L, ws, E, st, pos_apply);
+  }
   using G = Geo<T, D, NW, WITH_DH>;
   RowsArgs a;
   a.pos_apply = pos_apply;
@@ -1611,9 +2153,45 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   }
 }
 
+// dE sweep of bf16 D = 256 / 512 on the 16-owner engine (item tiles of 128, halved tail tiles as in items_launch).
+template <int D>
+static hipError_t items_launch16(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
+                                 hipStream_t st) {
+  ItemsArgs a;
+  a.Hc = ws + L.off_Hc;
+  a.Hrp = ws + L.off_Hrp;
+  a.E = E;
+  a.ctl = (const Ctl*)(ws + L.off_ctl);
+  a.bptr = (const int32_t*)(ws + L.off_bptr_i);
+  a.pairs = (const int2*)(ws + L.off_pairs_i);
+  a.sumH = (const double*)(ws + L.off_sumH);
+  a.grad_loss = grad_loss;
+  a.dE = dE;
+  a.V = L.V;
+  a.n_rs = L.n_rs;
+  a.R_pad = L.R_pad;
+  constexpr auto kern = k_items16<D>;
+  const size_t sm = Geo<__bf16, D, 8, true>::kLdsBytes;
+  int per_cu = 1;
+  hipError_t e = kernel_setup<kern>(512, sm, per_cu);
+  if (e != hipSuccess) return e;
+  const int64_t P = (int64_t)cu_count() * per_cu;
+  const int64_t rem = L.n_vt % P;
+  const int64_t n_split = (L.n_vt > P && rem > 0 && 2 * rem <= P) ? rem : 0;
+  a.n_full = (int)(L.n_vt - n_split);
+  a.tailpart = (float*)(ws + L.off_dhpart);
+  if (L.items_per_wg != 128 || n_split * 2 > L.part_rows / 128) return hipErrorInvalidValue;  // cannot happen
+  hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(512), sm, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || n_split == 0) return e;
+  hipLaunchKernelGGL((k_items_tail<__bf16, 128, D>), dim3((128 * D) / 1024, (unsigned)n_split), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int NW>
 static hipError_t items_launch(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                                hipStream_t st) {
+  if constexpr (narrow_owner(sizeof(T) == 2 ? 1 : 0, D)) return items_launch16<D>(L, ws, E, grad_loss, dE, st);
   using G = Geo<T, D, NW, true>;
   ItemsArgs a;
   a.Hc = ws + L.off_Hc;
