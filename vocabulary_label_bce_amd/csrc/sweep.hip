@@ -1692,9 +1692,18 @@ struct Epi8 {
   }
 };
 
-template <int D, bool FWD, bool GRAD, bool MET, int NW = 8, bool POS = !FWD || MET || !kGatherPositives>
+// PAIR (forward, D = 512): waves 2p and 2p + 1 own the same 16 rows and split the features: wave 2p + s holds
+// the owner operand and the dH accumulators of d in [s D/2, (s + 1) D/2), so each forms a partial logit tile over
+// its half. The partials go through LDS (two slots per wave, written in iteration i for step i + 1 and read after
+// the barrier of iteration i + 1) and both waves add them in the same order (half 0's + half 1's), so both hold
+// the same logits and G tile. 96 registers per wave instead of 192 give two waves per SIMD without spilling, and
+// no MFMA is repeated; the epilogue is computed by both waves.
+template <int D, bool FWD, bool GRAD, bool MET, int NW = 8, bool PAIR = false,
+          bool POS = !FWD || MET || !kGatherPositives>
 struct Eng16 {
   static constexpr int KB = D / 32, NDB = D / 16;
+  static constexpr int KBW = PAIR ? KB / 2 : KB, NDBW = PAIR ? NDB / 2 : NDB;  // this wave's k- and d-blocks
+  static_assert(!PAIR || (FWD && !POS && NW == 8), "paired waves: the forward without positives");
   // One wave per SIMD (NW = 4): the epilogue's stages are dealt out between the MFMAs and the whole order is
   // pinned, since no other wave fills the vector ALU; two waves per SIMD (NW = 8): the compiler places the
   // vector work between the pinned MFMAs and LDS reads.
@@ -1707,7 +1716,32 @@ struct Eng16 {
   };
   R r;
   bool apply_pos = true;
-  __device__ inline void setup(char* l, int w, int ln) { r.setup(l, w, ln); }
+  int half = 0;        // PAIR: this wave's feature half
+  uint32_t xoff = 0;   // PAIR: LDS byte offset of the partial-logit exchange (2 slots x NW waves x 2 KB)
+  static constexpr int kXchgBytes = PAIR ? 2 * NW * 64 * 32 : 0;
+  __device__ inline void setup(char* l, int w, int ln) {
+    r.setup(l, w, ln);
+    half = PAIR ? r.wave % 2 : 0;
+    xoff = (G::kNA + G::kNB) * G::kStepBytes;
+  }
+  static constexpr size_t lds_bytes() {
+    return PAIR ? (size_t)(G::kNA + G::kNB) * G::kStepBytes + kXchgBytes : (size_t)G::kLdsBytes;
+  }
+  // PAIR: this wave's partial logits of a step into exchange slot `slot`; the full tile from the two partials
+  __device__ inline void put_partial(int slot, const Z& z) const {
+    f32x4* x = (f32x4*)(r.lds + xoff + ((slot * NW + r.wave) * 64 + r.lane) * 32);
+    x[0] = z.h[0];
+    x[1] = z.h[1];
+  }
+  __device__ inline void full_logits(int slot, const Z& mine, float* zf) const {
+    const f32x4* x = (const f32x4*)(r.lds + xoff + ((slot * NW + (r.wave ^ 1)) * 64 + r.lane) * 32);
+    const f32x4 o0 = x[0], o1 = x[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      zf[q] = half == 0 ? mine.h[0][q] + o0[q] : o0[q] + mine.h[0][q];
+      zf[4 + q] = half == 0 ? mine.h[1][q] + o1[q] : o1[q] + mine.h[1][q];
+    }
+  }
 
   // The A ring holds each step's block operand-major: the 1 KB at (2 kb + h) * 1024 is the A operand of k-block
   // kb, half h, lane l's 16 bytes at l * 16 (streamed row 16h + l%16, features 32 kb + 8 (l/16) .. + 7). The DMA
@@ -1783,10 +1817,10 @@ struct Eng16 {
   template <bool kL, bool kG, bool kE = false>
   __device__ inline void mfma_seq(int ia, int ig, const bf16x8* own, Z& zn, const GOp& g, f32x4* acc,
                                   EP* es = nullptr) const {
-    constexpr int NM = (kL ? 2 * KB : 0) + (kG ? NDB : 0);
+    constexpr int NM = (kL ? 2 * KBW : 0) + (kG ? NDBW : 0);
     constexpr int PER = kE ? (NM / EP::NS > 0 ? NM / EP::NS : 1) : 1;  // MFMAs per epilogue stage
-    const char* pa = r.lds + (ia % G::kNA) * G::kStepBytes + r.lane * 16;
-    const char* pg = r.lds + (G::kNA + ig % (G::kNB ? G::kNB : 1)) * G::kStepBytes + r.lane * 16;
+    const char* pa = r.lds + (ia % G::kNA) * G::kStepBytes + r.lane * 16 + half * (KBW * 2 * 1024);
+    const char* pg = r.lds + (G::kNA + ig % (G::kNB ? G::kNB : 1)) * G::kStepBytes + r.lane * 16 + half * (NDBW * 1024);
     if (kL) {
       zn.h[0] = f32x4{};
       zn.h[1] = f32x4{};
@@ -1835,14 +1869,19 @@ struct Eng16 {
     int pb = 0, pe = 0;
     if (POS) r.bkt_get(i, pb, pe);
     EP es;
+    if (PAIR) {
+      full_logits(i % 2, zc, es.z);
+    } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) es.z[q] = zc.h[q / 4][q % 4];
+      for (int q = 0; q < 8; ++q) es.z[q] = zc.h[q / 4][q % 4];
+    }
     if (kStaged) {
       mfma_seq<NEXT, GRAD && PREV, true>(i + 1, i - 1, own, zn, g, acc, &es);
     } else {
       mfma_seq<NEXT, GRAD && PREV, false>(i + 1, i - 1, own, zn, g, acc);
       es.all_stages();
     }
+    if (PAIR && NEXT) put_partial((i + 1) % 2, zn);
     es.finish(e_acc);
     epilogue_end(i, pb, pe, es, g, posz, met);
   }
@@ -1858,9 +1897,11 @@ struct Eng16 {
     }
     if (POS) r.bkt_init();
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(!PAIR || G::kK == 1, "paired waves exchange partial logits across the barrier of every step");
     GOp g;
     Z zc, zn;
     mfma_seq<true, false>(0, 0, own, zc, g, acc);  // step 0
+    if (PAIR) put_partial(0, zc);
     if (n == 1) {
       iter<false, false>(0, own, zc, zn, g, acc, e_acc, posz, met);
     } else {
@@ -1880,10 +1921,10 @@ struct Eng16 {
 
 // Forward sweep on the 16-owner engine: the unit loop, splits and partial layouts of k_rows (row tiles of NW waves
 // x 16 rows: 128 at D = 256, two waves per SIMD; 64 at D = 512, one wave per SIMD).
-template <int D, bool WITH_DH, bool MET, int NW>
+template <int D, bool WITH_DH, bool MET, int NW, bool PAIR>
 __global__ void __launch_bounds__(NW * 64) k_rows16(RowsArgs a) {
-  using EN = Eng16<D, true, WITH_DH, MET, NW>;
-  constexpr int RW = NW * 16, KB = D / 32, NDB = D / 16;
+  using EN = Eng16<D, true, WITH_DH, MET, NW, PAIR>;
+  constexpr int RW = (PAIR ? NW / 2 : NW) * 16, KB = EN::KBW, NDB = EN::NDBW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   const __bf16* __restrict__ Hc = (const __bf16*)a.Hc;
@@ -1908,14 +1949,15 @@ __global__ void __launch_bounds__(NW * 64) k_rows16(RowsArgs a) {
   for (int idx = slot; idx < cnt; idx += P / 8) {
     const int u = start + idx;
     const int s = u / Tt, t = u % Tt;
-    const int r_base = t * RW + wave * 16;
+    const int wrow = PAIR ? wave / 2 : wave;  // the wave's 16 rows within the tile
+    const int r_base = t * RW + wrow * 16;
     en.r.j0 = (int)(((int64_t)s * n_steps) / S);
     en.r.j1 = (int)(((int64_t)(s + 1) * n_steps) / S);
     en.r.bbase = (int64_t)t * a.n_vs;
     en.r.own0 = r_base;
     // lane addresses made opaque, so that the compiler does not hoist per-offset partial addresses out of the
     // unit loop (they would stay live across it)
-    const __bf16* hp = Hc + (int64_t)(r_base + lane % 16) * D + (lane / 16) * 8;
+    const __bf16* hp = Hc + (int64_t)(r_base + lane % 16) * D + en.half * (D / 2) + (lane / 16) * 8;
     asm volatile("" : "+v"(hp));
     bf16x8 hop[KB];
 #pragma unroll
@@ -1927,11 +1969,11 @@ __global__ void __launch_bounds__(NW * 64) k_rows16(RowsArgs a) {
     int met[3] = {0, 0, 0};
     en.run(hop, acc, e_acc, posz, met);
     // lanes o, o + 16, o + 32, o + 48 hold row o's sums
-    const int64_t urow = (int64_t)u * RW + wave * 16;
+    const int64_t urow = (int64_t)u * RW + wrow * 16;
     float e_tot = e_acc + __shfl_xor(e_acc, 16, 64), p_tot = posz + __shfl_xor(posz, 16, 64);
     e_tot += __shfl_xor(e_tot, 32, 64);
     p_tot += __shfl_xor(p_tot, 32, 64);
-    if (lane < 16) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    if (lane < 16 && en.half == 0) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
     if (MET) {
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
@@ -1941,7 +1983,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows16(RowsArgs a) {
       if (lane < 16) a.metpart[urow + lane] = make_int4(met[0], met[1], met[2], 0);
     }
     if (WITH_DH) {
-      float* dp = a.dhpart + (urow + 4 * (lane / 16)) * D + lane % 16;
+      float* dp = a.dhpart + (urow + 4 * (lane / 16)) * D + en.half * (D / 2) + lane % 16;
       asm volatile("" : "+v"(dp));
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -2089,11 +2131,14 @@ static RowsArgs rows_args(const Layout& L, char* ws, const void* E, bool pos_app
 // Forward sweep of bf16 D = 256 / 512 on the 16-owner engine (one pass; the same row tiles of 128 and partials).
 template <int D, bool WITH_DH, bool MET>
 static hipError_t rows_launch16(const Layout& L, char* ws, const void* E, hipStream_t st, bool pos_apply) {
-  constexpr int NW = rows16_waves(D);
-  if (L.rows_per_wg != NW * 16) return hipErrorInvalidValue;  // the layout's row tiles are this kernel's
+  // D = 512: paired waves (two per SIMD), or with Cut Metrics (which needs the positives' mask area) one wave
+  // per SIMD over whole rows; both keep 64-row tiles
+  constexpr bool PAIR = D == 512 && !MET && !(!kGatherPositives);
+  constexpr int NW = PAIR ? 8 : rows16_waves(D);
+  if (L.rows_per_wg != (PAIR ? NW / 2 : NW) * 16) return hipErrorInvalidValue;  // the layout's row tiles
   const RowsArgs a = rows_args(L, ws, E, pos_apply, 0);
-  constexpr auto kern = k_rows16<D, WITH_DH, MET, NW>;
-  const size_t sm = Geo<__bf16, D, NW, WITH_DH>::kLdsBytes;
+  constexpr auto kern = k_rows16<D, WITH_DH, MET, NW, PAIR>;
+  const size_t sm = Eng16<D, true, WITH_DH, MET, NW, PAIR>::lds_bytes();
   int per_cu = 1;
   hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
   if (e != hipSuccess) return e;
