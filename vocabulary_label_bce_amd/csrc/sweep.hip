@@ -1833,7 +1833,9 @@ struct Eng16 {
     auto read = [&](int k) -> u32x4 {
       return is_l(k) ? *(const u32x4*)(pa + (2 * l_kb(k) + l_h(k)) * 1024) : *(const u32x4*)(pg + g_db(k) * 1024);
     };
-    constexpr int RB = NW == 4 ? 6 : 4;  // operand ring: reads RB - 1 MFMAs ahead
+    // operand ring, reads RB - 1 MFMAs ahead; measured: 6 for the D = 256 forward (-6.5% at 4,096 rows x 10M
+    // items), no gain for the dE sweeps or the paired D = 512 forward
+    constexpr int RB = (NW == 4 || (FWD && D == 256)) ? 6 : 4;
     u32x4 buf[RB];
 #pragma unroll
     for (int k = 0; k < RB - 1; ++k)
