@@ -2102,6 +2102,15 @@ constexpr bool two_pass() {
   return (D / 32) * 16 + (D / Elem<T>::kK) * (int)(sizeof(typename Elem<T>::Op) / 4) >= 256;
 }
 
+// Item tiles of the dE sweep swept by two workgroups over the two halves of the rows (k_items_tail adds the
+// halves): the tiles of the last round when it would be at most half full, or every tile when all of them fill at
+// most half of the P resident workgroups (at 6,400 rows x 100,000 items, 391 tiles of 256 items for 768 slots)
+// and the partial-sum area holds them (cap halved tiles).
+static int64_t halved_tiles(int64_t n_vt, int64_t P, int64_t rem, int64_t cap) {
+  if (n_vt > P) return (rem > 0 && 2 * rem <= P) ? rem : 0;
+  return 2 * n_vt <= P && n_vt <= cap ? n_vt : 0;
+}
+
 // Forward-sweep grid: persistent, as many workgroups as can be resident at once (per_cu per CU), a multiple of
 // 8 (one range per XCD). The kernel derives its vocabulary splits from the grid size.
 static int persistent_grid(int per_cu) {
@@ -2224,7 +2233,7 @@ static hipError_t items_launch16(const Layout& L, char* ws, const void* E, const
   if (e != hipSuccess) return e;
   const int64_t P = (int64_t)cu_count() * per_cu;
   const int64_t rem = L.n_vt % P;
-  const int64_t n_split = (L.n_vt > P && rem > 0 && 2 * rem <= P) ? rem : 0;
+  const int64_t n_split = halved_tiles(L.n_vt, P, rem, L.part_rows / 256);
   a.n_full = (int)(L.n_vt - n_split);
   a.tailpart = (float*)(ws + L.off_dhpart);
   if (L.items_per_wg != 128 || n_split * 2 > L.part_rows / 128) return hipErrorInvalidValue;  // cannot happen
@@ -2268,12 +2277,12 @@ static hipError_t items_launch(const Layout& L, char* ws, const void* E, const f
     if ((e = kernel_setup<kern2>(NW * 64, sm, c2)) != hipSuccess) return e;
     if (c2 < per_cu) per_cu = c2;
   }
-  // P workgroups run at once; when the last round would be at most half full, its tiles are halved. The
-  // partial sums go to the forward sweep's dH partial area, which is not in use during the backward dE sweep
-  // (it holds at least 1024 tiles' worth of rows x D floats; P <= 1024).
+  // P workgroups run at once; tiles halved as halved_tiles says. The partial sums go to the forward sweep's
+  // dH partial area, which is not in use during the backward dE sweep (it holds at least min(n_vt, 1024) tiles'
+  // worth of rows x D floats; P <= 1024).
   const int64_t P = (int64_t)cu_count() * per_cu;
   const int64_t rem = L.n_vt % P;
-  const int64_t n_split = (L.n_vt > P && rem > 0 && 2 * rem <= P) ? rem : 0;
+  const int64_t n_split = halved_tiles(L.n_vt, P, rem, L.part_rows / (NW * 32) / 2);
   a.n_full = (int)(L.n_vt - n_split);
   a.tailpart = (float*)(ws + L.off_dhpart);
   if (n_split * 2 > (L.part_rows / (NW * 32))) return hipErrorInvalidValue;  // cannot happen: P <= 1024
