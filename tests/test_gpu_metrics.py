@@ -81,8 +81,11 @@ def test_metrics_match_oracle(name, kw):
     _check(p, got, ref, np.arange(kw["R"]))
 
 
-def test_metrics_leave_other_outputs_unchanged():
-    p = W.custom_problem(300, 3000, 128, dtype="bf16", seed=31, h_std=0.4, e_std=0.4, pos_per_row=(1, 8),
+@pytest.mark.parametrize("D", [128, 256, 512])
+def test_metrics_leave_other_outputs_unchanged(D):
+    # at D = 512 the two calls run different forward kernels (one wave per SIMD with Cut Metrics, paired waves
+    # without), which must still agree bit for bit
+    p = W.custom_problem(300, 3000, D, dtype="bf16", seed=31, h_std=0.4, e_std=0.4, pos_per_row=(1, 8),
                          mask_frac=0.2, dup_frac=0.2)
     a = _forward(p, metrics=True)
     b = _forward(p, metrics=False)

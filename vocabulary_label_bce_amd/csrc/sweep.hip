@@ -1821,9 +1821,14 @@ struct Eng16 {
     constexpr int PER = kE ? (NM / EP::NS > 0 ? NM / EP::NS : 1) : 1;  // MFMAs per epilogue stage
     const char* pa = r.lds + (ia % G::kNA) * G::kStepBytes + r.lane * 16 + half * (KBW * 2 * 1024);
     const char* pg = r.lds + (G::kNA + ig % (G::kNB ? G::kNB : 1)) * G::kStepBytes + r.lane * 16 + half * (NDBW * 1024);
+    // The one-wave D = 512 forward (Cut Metrics) sums its logits over the two feature halves separately and adds
+    // the halves, as the paired waves do, so that both forms give the same bits.
+    constexpr bool kHalves = FWD && D == 512 && !PAIR;
+    Z zx;  // kHalves: the second feature half
     if (kL) {
       zn.h[0] = f32x4{};
       zn.h[1] = f32x4{};
+      if (kHalves) zx = zn;
     }
     // MFMA k: logit (k-block, half) or gradient (d-block)
     auto is_l = [](int k) { return kL && (!kG || (k & 1) == 0); };
@@ -1846,8 +1851,12 @@ struct Eng16 {
       const u32x4 op = buf[k % RB];
       if (is_l(k)) {
         const int h = l_h(k);
-        zn.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), own[l_kb(k)], zn.h[h],
-                                                          0, 0, 0);
+        if (kHalves && l_kb(k) >= KB / 2)
+          zx.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), own[l_kb(k)], zx.h[h],
+                                                            0, 0, 0);
+        else
+          zn.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, op), own[l_kb(k)], zn.h[h],
+                                                            0, 0, 0);
       } else if constexpr (FWD) {
         acc[g_db(k)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g, __builtin_bit_cast(bf16x8, op), acc[g_db(k)], 0, 0,
                                                                0);
@@ -1861,6 +1870,10 @@ struct Eng16 {
     if (kE && NM / PER < EP::NS) {  // stages left over (a sequence shorter than the epilogue)
 #pragma unroll
       for (int st = NM / PER; st < EP::NS; ++st) es->stage(st);
+    }
+    if (kHalves && kL) {
+      zn.h[0] = zn.h[0] + zx.h[0];
+      zn.h[1] = zn.h[1] + zx.h[1];
     }
   }
   template <bool NEXT, bool PREV>
