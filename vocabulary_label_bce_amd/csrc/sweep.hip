@@ -343,10 +343,9 @@ __device__ inline void epi_items(const f32x16& z, uint32_t pm, float* c) {
 // Runs steps [j0, j1) of 32 streamed rows; bucket pointers of step j are bptr[bbase + j], bptr[bbase + j + 1].
 // Two schedules, both with the gradient GEMM of step i-1 (on the G tile packed in iteration i-1) in iteration i:
 //  - kPrefetch (the A operands of a step fit in 32 registers per lane: bf16 D <= 128, f32 D <= 64; also the
-//    bf16 D = 512 forward, whose one wave per SIMD has 512 registers: its 128 registers of A operands spill
-//    about 35 others, and still save 17% against reading each operand next to its MFMA, 4.56 vs 5.51 ms at
-//    4,096 rows x 262,144 items): iteration i runs the logit GEMM of step i on A operands read from LDS
-//    during iteration i-1, reads those of step i+1, and evaluates the epilogue of step i;
+//    bf16 D = 512 scoring sweep, whose one wave per SIMD has 512 registers): iteration i runs the logit GEMM of
+//    step i on A operands read from LDS during iteration i-1, reads those of step i+1, and evaluates the
+//    epilogue of step i;
 //  - otherwise the logit GEMM of step i+1 runs in iteration i with its A operands read next to each MFMA, two
 //    logit tiles alternating, and the epilogue of step i uses the tile formed in iteration i-1.
 // Ring loads, their slots and the barrier every kK iterations follow Geo; bucket pointers come 64 steps at a
@@ -1236,7 +1235,7 @@ struct RowsArgs {
 // part of E. With KT > 0 it scores instead: per-lane top-KT lists, merged per row and written per unit.
 // ---------------------------------------------------------------------------------------------------------
 // DHPART 0: one pass (loss, dH and optional Cut Metrics); 1 / 2: the first / second of two passes, each
-// accumulating half of dH's d-blocks (half the accumulator registers, for D = 512); the loss and the Cut
+// accumulating half of dH's d-blocks (half the accumulator registers, for f32 D = 256); the loss and the Cut
 // Metrics come from pass 1.
 template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT, int DHPART = 0>
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
@@ -1378,7 +1377,7 @@ struct ItemsArgs {
 // Backward dE sweep: workgroup = item tile (32 items per wave), sweeping all valid rows.
 // ---------------------------------------------------------------------------------------------------------
 // DEPART 0: one pass; 1 / 2: the first / second of two passes, each accumulating and writing half of dE's
-// d-blocks (half the accumulator registers, for D = 512).
+// d-blocks (half the accumulator registers, for f32 D = 256).
 template <typename T, int D, int NW, int DEPART = 0>
 __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
   using EL = Elem<T>;
@@ -2107,9 +2106,9 @@ static hipError_t kernel_setup(int threads, size_t sm, int& per_cu) {
 }
 
 // Gradient accumulators (NDB tiles of 16 registers) plus the owner operand (D / k-per-MFMA operands) per lane:
-// when they fill the 256 registers of a wave, the sweep can run as two passes over half of the gradient's
-// d-blocks each (bf16 D = 512, f32 D = 256), recomputing the logits instead of spilling. Measured, forward:
-// bf16 D = 512 4.95 -> 2.47 ms, f32 D = 256 26.4 -> 17.2 ms (4,096 rows, 131,072 items).
+// when they fill the 256 registers of a wave, the 32-owner sweeps can run as two passes over half of the
+// gradient's d-blocks each, recomputing the logits instead of spilling: used for f32 D = 256 (forward 26.4 ->
+// 17.2 ms at 4,096 rows x 131,072 items); bf16 D = 256 and 512 run the 16-owner engine instead.
 template <typename T, int D>
 constexpr bool two_pass() {
   return (D / 32) * 16 + (D / Elem<T>::kK) * (int)(sizeof(typename Elem<T>::Op) / 4) >= 256;
@@ -2175,50 +2174,34 @@ static hipError_t rows_launch(const Layout& L, char* ws, const void* E, hipStrea
   if constexpr (KT == 0 && narrow_owner(sizeof(T) == 2 ? 1 : 0, D)) {
     static_assert(NW * 32 == rows16_waves(D) * 16, "the scoring engine and the 16-owner engine share row tiles");
     return rows_launch16<D, WITH_DH, MET>(L, ws, E, st, pos_apply);
-  }
-  using G = Geo<T, D, NW, WITH_DH>;
-  RowsArgs a;
-  a.pos_apply = pos_apply;
-  a.Hc = ws + L.off_Hc;
-  a.E = E;
-  a.Evp = ws + L.off_Evp;
-  a.ctl = (Ctl*)(ws + L.off_ctl);
-  a.bptr = (const int32_t*)(ws + L.off_bptr_r);
-  a.pairs = (const int2*)(ws + L.off_pairs_r);
-  a.V = L.V;
-  a.V_pad = L.V_pad;
-  a.n_vs = L.n_vs;
-  a.R_pad = L.R_pad;
-  a.dhpart = (float*)(ws + L.off_dhpart);
-  a.rowpart = (float2*)(ws + L.off_rowpart);
-  a.metpart = (int4*)(ws + L.off_metpart);
-  // scoring partials reuse the dH partial area: KT * 8 bytes per row <= D * 4 bytes
-  static_assert(KT * 8 <= D * 4, "top-k partials fit in the dH partial area");
-  a.topv = (float*)(ws + L.off_dhpart);
-  a.topi = (int32_t*)(ws + L.off_dhpart) + (size_t)L.part_rows * (KT ? KT : 1);
-  const size_t sm = G::kLdsBytes;
-  // Both passes run on the same grid, hence the same vocabulary splits and partial-sum layout.
-  constexpr bool kTwoPass = WITH_DH && KT == 0 && two_pass<T, D>();
-  if constexpr (kTwoPass) {
-    constexpr auto k1 = k_rows<T, D, NW, WITH_DH, MET, KT, 1>;
-    constexpr auto k2 = k_rows<T, D, NW, WITH_DH, false, KT, 2>;
-    int c1 = 1, c2 = 1;
-    hipError_t e = kernel_setup<k1>(NW * 64, sm, c1);
-    if (e != hipSuccess) return e;
-    if ((e = kernel_setup<k2>(NW * 64, sm, c2)) != hipSuccess) return e;
-    const int P = persistent_grid(c1 < c2 ? c1 : c2);
-    hipLaunchKernelGGL(k1, dim3(P), dim3(NW * 64), sm, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k2, dim3(P), dim3(NW * 64), sm, st, a);
-    return hipGetLastError();
   } else {
-    constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
-    const size_t sm1 = sweep_lds<T, D, NW, true, WITH_DH, MET, KT, 0>();
-    int per_cu = 1;
-    hipError_t e = kernel_setup<kern>(NW * 64, sm1, per_cu);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm1, st, a);
-    return hipGetLastError();
+    // scoring partials reuse the dH partial area: KT * 8 bytes per row <= D * 4 bytes
+    static_assert(KT * 8 <= D * 4, "top-k partials fit in the dH partial area");
+    const RowsArgs a = rows_args(L, ws, E, pos_apply, KT);
+    // Both passes run on the same grid, hence the same vocabulary splits and partial-sum layout.
+    constexpr bool kTwoPass = WITH_DH && KT == 0 && two_pass<T, D>();
+    if constexpr (kTwoPass) {
+      const size_t sm = Geo<T, D, NW, WITH_DH>::kLdsBytes;
+      constexpr auto k1 = k_rows<T, D, NW, WITH_DH, MET, KT, 1>;
+      constexpr auto k2 = k_rows<T, D, NW, WITH_DH, false, KT, 2>;
+      int c1 = 1, c2 = 1;
+      hipError_t e = kernel_setup<k1>(NW * 64, sm, c1);
+      if (e != hipSuccess) return e;
+      if ((e = kernel_setup<k2>(NW * 64, sm, c2)) != hipSuccess) return e;
+      const int P = persistent_grid(c1 < c2 ? c1 : c2);
+      hipLaunchKernelGGL(k1, dim3(P), dim3(NW * 64), sm, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(k2, dim3(P), dim3(NW * 64), sm, st, a);
+      return hipGetLastError();
+    } else {
+      constexpr auto kern = k_rows<T, D, NW, WITH_DH, MET, KT>;
+      const size_t sm1 = sweep_lds<T, D, NW, true, WITH_DH, MET, KT, 0>();
+      int per_cu = 1;
+      hipError_t e = kernel_setup<kern>(NW * 64, sm1, per_cu);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(persistent_grid(per_cu)), dim3(NW * 64), sm1, st, a);
+      return hipGetLastError();
+    }
   }
 }
 
@@ -2260,55 +2243,58 @@ static hipError_t items_launch16(const Layout& L, char* ws, const void* E, const
 template <typename T, int D, int NW>
 static hipError_t items_launch(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                                hipStream_t st) {
-  if constexpr (narrow_owner(sizeof(T) == 2 ? 1 : 0, D)) return items_launch16<D>(L, ws, E, grad_loss, dE, st);
-  using G = Geo<T, D, NW, true>;
-  ItemsArgs a;
-  a.Hc = ws + L.off_Hc;
-  a.Hrp = ws + L.off_Hrp;
-  a.E = E;
-  a.ctl = (const Ctl*)(ws + L.off_ctl);
-  a.bptr = (const int32_t*)(ws + L.off_bptr_i);
-  a.pairs = (const int2*)(ws + L.off_pairs_i);
-  a.sumH = (const double*)(ws + L.off_sumH);
-  a.grad_loss = grad_loss;
-  a.dE = dE;
-  a.V = L.V;
-  a.n_rs = L.n_rs;
-  a.R_pad = L.R_pad;
-  const size_t sm = two_pass<T, D>() && sizeof(T) == 4 ? G::kLdsBytes
-                                                        : sweep_lds<T, D, NW, false, true, false, 0, 0>();
-  // Two passes (see two_pass) run on the same grid and tail split. Measured: f32 D = 256 (the single pass
-  // spills ~300 registers) 8.3 vs 21 ms; bf16 D = 512 (~100 spilled) is faster in one pass, 1.87 vs 2.03 ms.
-  constexpr bool kTwoPass = two_pass<T, D>() && sizeof(T) == 4;
-  constexpr auto kern = k_items<T, D, NW, kTwoPass ? 1 : 0>;
-  constexpr auto kern2 = k_items<T, D, NW, kTwoPass ? 2 : 0>;
-  int per_cu = 1;
-  hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
-  if (e != hipSuccess) return e;
-  if (kTwoPass) {
-    int c2 = 1;
-    if ((e = kernel_setup<kern2>(NW * 64, sm, c2)) != hipSuccess) return e;
-    if (c2 < per_cu) per_cu = c2;
-  }
-  // P workgroups run at once; tiles halved as halved_tiles says. The partial sums go to the forward sweep's
-  // dH partial area, which is not in use during the backward dE sweep (it holds at least min(n_vt, 1024) tiles'
-  // worth of rows x D floats; P <= 1024).
-  const int64_t P = (int64_t)cu_count() * per_cu;
-  const int64_t rem = L.n_vt % P;
-  const int64_t n_split = halved_tiles(L.n_vt, P, rem, L.part_rows / (NW * 32) / 2);
-  a.n_full = (int)(L.n_vt - n_split);
-  a.tailpart = (float*)(ws + L.off_dhpart);
-  if (n_split * 2 > (L.part_rows / (NW * 32))) return hipErrorInvalidValue;  // cannot happen: P <= 1024
-  hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
-  e = hipGetLastError();
-  if (e == hipSuccess && kTwoPass) {
-    hipLaunchKernelGGL(kern2, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
+  if constexpr (narrow_owner(sizeof(T) == 2 ? 1 : 0, D)) {
+    return items_launch16<D>(L, ws, E, grad_loss, dE, st);
+  } else {
+    using G = Geo<T, D, NW, true>;
+    ItemsArgs a;
+    a.Hc = ws + L.off_Hc;
+    a.Hrp = ws + L.off_Hrp;
+    a.E = E;
+    a.ctl = (const Ctl*)(ws + L.off_ctl);
+    a.bptr = (const int32_t*)(ws + L.off_bptr_i);
+    a.pairs = (const int2*)(ws + L.off_pairs_i);
+    a.sumH = (const double*)(ws + L.off_sumH);
+    a.grad_loss = grad_loss;
+    a.dE = dE;
+    a.V = L.V;
+    a.n_rs = L.n_rs;
+    a.R_pad = L.R_pad;
+    const size_t sm = two_pass<T, D>() && sizeof(T) == 4 ? G::kLdsBytes
+                                                          : sweep_lds<T, D, NW, false, true, false, 0, 0>();
+    // Two passes (see two_pass) run on the same grid and tail split. Measured: f32 D = 256 (the single pass
+    // spills ~300 registers) 8.3 vs 21 ms.
+    constexpr bool kTwoPass = two_pass<T, D>() && sizeof(T) == 4;
+    constexpr auto kern = k_items<T, D, NW, kTwoPass ? 1 : 0>;
+    constexpr auto kern2 = k_items<T, D, NW, kTwoPass ? 2 : 0>;
+    int per_cu = 1;
+    hipError_t e = kernel_setup<kern>(NW * 64, sm, per_cu);
+    if (e != hipSuccess) return e;
+    if (kTwoPass) {
+      int c2 = 1;
+      if ((e = kernel_setup<kern2>(NW * 64, sm, c2)) != hipSuccess) return e;
+      if (c2 < per_cu) per_cu = c2;
+    }
+    // P workgroups run at once; tiles halved as halved_tiles says. The partial sums go to the forward sweep's
+    // dH partial area, which is not in use during the backward dE sweep (it holds at least min(n_vt, 1024) tiles'
+    // worth of rows x D floats; P <= 1024).
+    const int64_t P = (int64_t)cu_count() * per_cu;
+    const int64_t rem = L.n_vt % P;
+    const int64_t n_split = halved_tiles(L.n_vt, P, rem, L.part_rows / (NW * 32) / 2);
+    a.n_full = (int)(L.n_vt - n_split);
+    a.tailpart = (float*)(ws + L.off_dhpart);
+    if (n_split * 2 > (L.part_rows / (NW * 32))) return hipErrorInvalidValue;  // cannot happen: P <= 1024
+    hipLaunchKernelGGL(kern, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
     e = hipGetLastError();
+    if (e == hipSuccess && kTwoPass) {
+      hipLaunchKernelGGL(kern2, dim3((unsigned)(L.n_vt + n_split)), dim3(NW * 64), sm, st, a);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess || n_split == 0) return e;
+    hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((NW * 32 * D) / 1024, (unsigned)n_split), dim3(256), 0, st,
+                       a);
+    return hipGetLastError();
   }
-  if (e != hipSuccess || n_split == 0) return e;
-  hipLaunchKernelGGL((k_items_tail<T, NW * 32, D>), dim3((NW * 32 * D) / 1024, (unsigned)n_split), dim3(256), 0, st,
-                     a);
-  return hipGetLastError();
 }
 
 #define CUTBCE_DISPATCH(DT, FN, ...)                                                             \
