@@ -15,7 +15,7 @@ def _args(p, H, E):
     return (H, E, p["row_offsets"].cuda(), p["item_ids"].cuda(), p["row_mask"].cuda())
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 256), ("bf16", 512)])
 def test_graph_replays_match_eager(dtype, D):
     p = W.custom_problem(300, 5000, D, dtype=dtype, seed=41, h_std=0.3, e_std=0.3, pos_per_row=(1, 8),
                          mask_frac=0.2)
