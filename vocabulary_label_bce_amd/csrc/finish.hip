@@ -62,20 +62,33 @@ __device__ inline void gather_positives(const int2* __restrict__ rptr, const int
       keep = keep & !(j < lane && u == v);
     }
     uint64_t m = __ballot(keep);
-    while (m) {  // uniform: up to ng positives per round, one per group
-      int src = -1;
-      for (int gg = 0; gg < ng && m; ++gg) {
-        const int b = __builtin_ctzll(m);
-        m &= m - 1;
-        if (g == gg) src = b;
-      }
-      const int vv = __shfl(v, src < 0 ? 0 : src, 64);
-      if (src >= 0) {
-        const u32x4 raw = *(const u32x4*)(E + (int64_t)vv * D + sub * EPL);
-        const T* x = (const T*)&raw;
+    while (m) {  // uniform: kRounds rounds of up to ng positives each (one per group), their loads issued together
+      constexpr int kRounds = 8;
+      int vv[kRounds];
+      bool has[kRounds];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += (float)x[e];
+      for (int u = 0; u < kRounds; ++u) {
+        int src = -1;
+        for (int gg = 0; gg < ng && m; ++gg) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          if (g == gg) src = b;
+        }
+        vv[u] = __shfl(v, src < 0 ? 0 : src, 64);
+        has[u] = src >= 0;
       }
+      u32x4 raw[kRounds];
+#pragma unroll
+      for (int u = 0; u < kRounds; ++u)
+        raw[u] = has[u] ? *(const u32x4*)(E + (int64_t)vv[u] * D + sub * EPL) : u32x4{0u, 0u, 0u, 0u};
+      // added round by round: each group takes its positives in row order, as one round at a time would
+#pragma unroll
+      for (int u = 0; u < kRounds; ++u)
+        if (has[u]) {
+          const T* x = (const T*)&raw[u];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += (float)x[e];
+        }
     }
   }
   // the groups' sums, added in group order
@@ -126,9 +139,20 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
   for (int i = 0; i < 8; ++i) Sp[i] = 0.f;
   if (E) gather_positives<T>(rptr, ids, E, V, D, k, lane, sh_pos[threadIdx.x / 64], Sp);
   if (dh_out) {
+    // split s's partial of (row tile t, row loc) sits at ((s Tt + t) RW + loc) D; the splits are added in order,
+    // eight loads issued before their adds
+    const int64_t stride = (int64_t)Tt * RW * D;
     for (int i = 0, d = lane; d < D; ++i, d += 64) {
+      const float* src = dhpart + ((int64_t)t * RW + loc) * D + d;
       double acc = 0.0;
-      for (int s = 0; s < S; ++s) acc += (double)dhpart[((int64_t)(s * Tt + t) * RW + loc) * D + d];
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)min(s0 + j, S - 1) * stride];  // past S: unused
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s0 + j < S) acc += (double)x[j];
+      }
       dh_out[r * D + d] = (float)(sw * (acc + 0.5 * sumE[d] - (double)Sp[i]));
     }
   }
@@ -139,10 +163,14 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
     p += q.y;
   }
   double zs = 0.0, pg = 0.0;
-  for (int i = 0, d = lane; d < D; ++i, d += 64) {
-    const double h = (double)(float)H[r * D + d];
-    zs += h * sumE[d];
-    pg += h * (double)Sp[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // d = lane + 64 i < D <= 512
+    const int d = lane + 64 * i;
+    if (d < D) {
+      const double h = (double)(float)H[r * D + d];
+      zs += h * sumE[d];
+      pg += h * (double)Sp[i];
+    }
   }
   e = wave_sum(e);
   p = wave_sum(p) + wave_sum(pg);

@@ -413,15 +413,28 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
   const int upr = D * (int)sizeof(T) / 16;
   double acc0 = 0.0, acc1 = 0.0;  // column sums for d = tid and d = tid + 256
   const int64_t v_begin = (int64_t)blockIdx.x * kEBlkItems;
+  // the 16-byte units of a 32-item chunk, unit u = tid + 256 q (at most 8 per thread: D * sizeof(T) <= 1024);
+  // the next chunk's units are loaded while the current one is packed
+  constexpr int kMaxU = 8;
+  u32x4 nx[kMaxU];
+  auto load_chunk = [&](int64_t v0) {
+#pragma unroll
+    for (int q = 0; q < kMaxU; ++q) {
+      const int u = tid + 256 * q, rr = u / upr, c = u % upr;
+      nx[q] = u32x4{0u, 0u, 0u, 0u};
+      if (u < 32 * upr && v0 + rr < V) nx[q] = *(const u32x4*)((const char*)E + ((v0 + rr) * D) * sizeof(T) + c * 16);
+    }
+  };
+  load_chunk(v_begin);
   for (int ch = 0; ch < kEBlkItems / 32; ++ch) {
     const int64_t v0 = v_begin + ch * 32;
-    for (int u = tid; u < 32 * upr; u += 256) {
-      const int rr = u / upr, c = u % upr;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (v0 + rr < V) x = *(const u32x4*)((const char*)E + ((v0 + rr) * D) * sizeof(T) + c * 16);
-      *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = x;
+#pragma unroll
+    for (int q = 0; q < kMaxU; ++q) {
+      const int u = tid + 256 * q, rr = u / upr, c = u % upr;
+      if (u < 32 * upr) *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = nx[q];
     }
     __syncthreads();
+    if (ch + 1 < kEBlkItems / 32) load_chunk(v0 + 32);
     bool packed = false;
     if constexpr (sizeof(T) == 2) {
       if (Evp && narrow_owner(1, D)) {
