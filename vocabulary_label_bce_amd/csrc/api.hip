@@ -77,6 +77,7 @@ Layout make_layout(const cutbce_problem* p) {
   L.off_sumH_part = take(sizeof(double) * L.D * (L.R_pad / 32));
   L.off_sumE = take(sizeof(double) * L.D);
   L.off_sumE_part = take(sizeof(double) * L.D * L.n_eblk);
+  L.off_sum2 = take(sizeof(double) * L.D * kSumMaxGroups);
   L.off_Evp = take((size_t)L.V_pad * L.D * L.esz);
   L.off_dhpart = take(sizeof(float) * (size_t)part_rows * L.D);
   L.off_rowpart = take(sizeof(float) * 2 * (size_t)part_rows);

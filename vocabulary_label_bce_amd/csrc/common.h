@@ -111,7 +111,7 @@ struct Layout {
   int64_t n_eblk;     // blocks of the E preparation kernel
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
-  size_t off_sumE, off_sumE_part, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
+  size_t off_sumE, off_sumE_part, off_sum2, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan, off_cpart;
   size_t scan_elems;
   int64_t part_rows;  // rows of the forward sweep's unit-major partial buffers
@@ -128,6 +128,7 @@ constexpr bool kGatherPositives = CUTBCE_GATHER_POSITIVES != 0;
 
 constexpr int kEBlkItems = 256;   // items per block of the E preparation kernel (column-sum granularity)
 constexpr int kScanBlock = 8192;  // elements per block of the multi-block scan
+constexpr int kSumMaxGroups = 64;  // part groups of the two-pass column sums (group sums: kSumMaxGroups x D doubles)
 
 // Waves per workgroup of the 32-owner sweeps for a (dtype, D); a workgroup's row tile (and, except for the
 // 16-owner dE sweep, item tile) is 32 of these. bf16 D = 512: only the scoring sweep runs on it, with the row tiles
@@ -163,7 +164,8 @@ hipError_t launch_rows_sweep(const Layout& L, char* ws, const void* E, bool with
 hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const uint8_t* mask, float* loss,
                               float* row_loss, float* dh_out, bool with_dh, int32_t* metrics, const void* E,
                               const int32_t* item_ids, hipStream_t st);
-// Bucket pointers of the forward sweep set to zero: every bucket empty, the sweep sees no positives.
+// Bucket pointers of the forward sweep set to zero (every bucket empty, the sweep sees no positives) for the
+// sweeps that read them; the bf16 forward sweeps without Cut Metrics read none, and nothing is launched for them.
 hipError_t launch_no_row_buckets(const Layout& L, char* ws, hipStream_t st);
 hipError_t launch_items_sweep(const Layout& L, char* ws, const void* E, const float* grad_loss, void* dE,
                               hipStream_t st);

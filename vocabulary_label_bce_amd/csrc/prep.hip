@@ -22,12 +22,6 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-// Plain int copy as a kernel (a kernel node when the caller captures the stream into a graph).
-__global__ void k_copy_i32(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    dst[i] = src[i];
-}
-
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -337,33 +331,70 @@ __global__ void __launch_bounds__(256) k_prep_hrp16(const __bf16* __restrict__ H
   }
 }
 
-// Sum `nparts` rows of float64 partials [nparts][D] in a fixed order: block = 32 columns x 32 part lanes; part
-// lane y adds parts y + 32 m for m = 0, 1, ... into four running sums (m mod 4, so four loads are in flight),
-// adds those four, then the 32 lane sums are added in order of y.
+// Column sums of `nparts` rows of float64 partials [nparts][D], in a fixed order, in one or two passes. The
+// parts form G groups of `per` consecutive parts (G from nparts alone: one group per 512 parts, at most
+// kSumMaxGroups). Pass 1, block (x, g): 16 columns x 64 part lanes; lane y adds parts y, y + 64, ... of group g
+// into four running sums (m mod 4, so four loads are in flight), adds those four, and the 64 lane sums of a
+// column are added in order of y. With one group that is the result; otherwise pass 2 adds the G group sums of
+// each column in group order.
+constexpr int kSumCols = 16, kSumLanes = 64, kSumPartsPerGroup = 512;
+
 __global__ void __launch_bounds__(1024) k_sum_parts(const double* __restrict__ part, int64_t nparts, int D,
-                                                    double* __restrict__ out) {
-  __shared__ double sh[32][33];
-  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
-  const int d = blockIdx.x * 32 + tx;
+                                                    int64_t per, double* __restrict__ out) {
+  __shared__ double sh[kSumLanes][kSumCols + 1];
+  const int c = threadIdx.x % kSumCols, y = threadIdx.x / kSumCols;
+  const int d = blockIdx.x * kSumCols + c;
+  const int64_t p0 = (int64_t)blockIdx.y * per;
+  const int64_t p1 = p0 + per < nparts ? p0 + per : nparts;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
   if (d < D) {
-    int64_t p = ty;
-    for (; p + 96 < nparts; p += 128) {
+    int64_t p = p0 + y;
+    for (; p + 3 * kSumLanes < p1; p += 4 * kSumLanes) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s[q] += part[(p + 32 * q) * D + d];
+      for (int q = 0; q < 4; ++q) s[q] += part[(p + q * kSumLanes) * D + d];
     }
     // at most three parts are left
-    if (p < nparts) s[0] += part[p * D + d];
-    if (p + 32 < nparts) s[1] += part[(p + 32) * D + d];
-    if (p + 64 < nparts) s[2] += part[(p + 64) * D + d];
+    if (p < p1) s[0] += part[p * D + d];
+    if (p + kSumLanes < p1) s[1] += part[(p + kSumLanes) * D + d];
+    if (p + 2 * kSumLanes < p1) s[2] += part[(p + 2 * kSumLanes) * D + d];
   }
-  sh[ty][tx] = (s[0] + s[1]) + (s[2] + s[3]);
+  sh[y][c] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
-  if (ty == 0 && d < D) {
+  if (y == 0 && d < D) {
     double t = 0.0;
-    for (int y = 0; y < 32; ++y) t += sh[y][tx];
-    out[d] = t;
+    for (int yy = 0; yy < kSumLanes; ++yy) t += sh[yy][c];
+    out[(int64_t)blockIdx.y * D + d] = t;
   }
+}
+
+__global__ void k_sum_groups(const double* __restrict__ gsum, int G, int D, double* __restrict__ out) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= D) return;
+  double t = 0.0;
+  for (int g0 = 0; g0 < G; g0 += 8) {  // eight loads in flight, added in group order
+    double x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = gsum[(int64_t)min(g0 + j, G - 1) * D + d];  // past G: unused
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (g0 + j < G) t += x[j];
+  }
+  out[d] = t;
+}
+
+static hipError_t sum_parts(const Layout& L, char* ws, const double* part, int64_t nparts, double* out,
+                            hipStream_t st) {
+  int64_t G = (nparts + kSumPartsPerGroup - 1) / kSumPartsPerGroup;
+  G = G < 1 ? 1 : (G > kSumMaxGroups ? kSumMaxGroups : G);
+  const int64_t per = (nparts + G - 1) / G;
+  double* gsum = (double*)(ws + L.off_sum2);  // [G][D] group sums
+  hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((L.D + kSumCols - 1) / kSumCols), (unsigned)G), dim3(1024), 0, st,
+                     part, nparts, L.D, per, G == 1 ? out : gsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || G == 1) return e;
+  hipLaunchKernelGGL(k_sum_groups, dim3((unsigned)((L.D + 255) / 256)), dim3(256), 0, st, (const double*)gsum, (int)G,
+                     L.D, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp, hipStream_t st) {
@@ -388,9 +419,7 @@ hipError_t launch_prep_h(const Layout& L, char* ws, const void* H, bool want_hrp
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (f16rp && (e = launch_prep_hrp(L, ws, H, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
-                     (const double*)(ws + L.off_sumH_part), nblk, L.D, (double*)(ws + L.off_sumH));
-  return hipGetLastError();
+  return sum_parts(L, ws, (const double*)(ws + L.off_sumH_part), nblk, (double*)(ws + L.off_sumH), st);
 }
 
 hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t st) {
@@ -482,24 +511,37 @@ hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_parts, dim3((L.D + 31) / 32), dim3(1024), 0, st,
-                     (const double*)(ws + L.off_sumE_part), L.n_eblk, L.D, (double*)(ws + L.off_sumE));
-  return hipGetLastError();
+  return sum_parts(L, ws, (const double*)(ws + L.off_sumE_part), L.n_eblk, (double*)(ws + L.off_sumE), st);
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Multi-block exclusive scan of int32 counts, in place: x[i] <- sum_{j<i} x[j] for i <= n (x[n] = total).
+// Multi-block exclusive scan of int32 counts, in place: x[i] <- sum_{j<i} x[j] for i <= n (x[n] = total), and
+// optionally the scanned x[0..n) copied to `copy` as well. Thread t of block b owns the 8 entries from
+// b * kScanBlock + 8 t (one 32-byte run: two 16-byte loads and stores where the run lies inside [0, n)); entry n
+// (the grand total) falls in the first run that reaches past n - 1.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kScanPerThread = kScanBlock / 1024;
+static_assert(kScanPerThread == 8, "two 16-byte vectors per thread");
+
+__device__ inline void scan_load8(const int32_t* __restrict__ x, int64_t b0, int64_t n, int* v) {
+  if (b0 + 8 <= n) {
+    const int4 a = *(const int4*)(x + b0), b = *(const int4*)(x + b0 + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = b0 + j < n ? x[b0 + j] : 0;
+  }
+}
 
 __global__ void __launch_bounds__(1024) k_scan_sums(const int32_t* __restrict__ x, int64_t n,
                                                     int32_t* __restrict__ bsum) {
   __shared__ int sh[16];
   const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPerThread;
+  int v[8];
+  scan_load8(x, b0, n, v);
   int s = 0;
 #pragma unroll
-  for (int j = 0; j < kScanPerThread; ++j)
-    if (b0 + j < n) s += x[b0 + j];
+  for (int j = 0; j < 8; ++j) s += v[j];
   int tot;
   block_excl_scan(s, sh, tot);
   if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
@@ -523,31 +565,45 @@ __global__ void __launch_bounds__(1024) k_scan_bsums(int32_t* bsum, int64_t nb) 
 }
 
 __global__ void __launch_bounds__(1024) k_scan_apply(int32_t* __restrict__ x, int64_t n,
-                                                     const int32_t* __restrict__ bsum) {
+                                                     const int32_t* __restrict__ bsum, int32_t* __restrict__ copy) {
   __shared__ int sh[16];
   const int64_t b0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * kScanPerThread;
-  int v[kScanPerThread];
+  int v[8];
+  scan_load8(x, b0, n, v);
   int s = 0;
 #pragma unroll
-  for (int j = 0; j < kScanPerThread; ++j) {
-    v[j] = (b0 + j < n) ? x[b0 + j] : 0;
-    s += v[j];
-  }
+  for (int j = 0; j < 8; ++j) s += v[j];
   int tot;
   int run = block_excl_scan(s, sh, tot) + bsum[blockIdx.x];
+  int o[8];
 #pragma unroll
-  for (int j = 0; j < kScanPerThread; ++j) {
-    if (b0 + j <= n) x[b0 + j] = run;  // entry n receives the grand total
+  for (int j = 0; j < 8; ++j) {
+    o[j] = run;
     run += v[j];
+  }
+  if (b0 + 8 <= n) {
+    const int4 a = make_int4(o[0], o[1], o[2], o[3]), b = make_int4(o[4], o[5], o[6], o[7]);
+    *(int4*)(x + b0) = a;
+    *(int4*)(x + b0 + 4) = b;
+    if (copy) {
+      *(int4*)(copy + b0) = a;
+      *(int4*)(copy + b0 + 4) = b;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (b0 + j <= n) x[b0 + j] = o[j];  // entry n receives the grand total
+      if (copy && b0 + j < n) copy[b0 + j] = o[j];
+    }
   }
 }
 
-static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, hipStream_t st) {
+static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, int32_t* copy, hipStream_t st) {
   // n + 1 entries are written; blocks cover [0, n] inclusive
   const int64_t nb = (n + 1 + kScanBlock - 1) / kScanBlock;
   hipLaunchKernelGGL(k_scan_sums, dim3((unsigned)nb), dim3(1024), 0, st, x, n, tmp);
   hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(1024), 0, st, tmp, nb);
-  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(1024), 0, st, x, n, tmp);
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(1024), 0, st, x, n, (const int32_t*)tmp, copy);
   return hipGetLastError();
 }
 
@@ -686,12 +742,10 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
                        (int2*)nullptr, &ctl->bad_ids);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = scan_exclusive(bptr, nb, (int32_t*)(ws + L.off_scan), st)) != hipSuccess) return e;
+  // the scan also leaves the bucket starts in bfill, the scatter's running counters
+  if ((e = scan_exclusive(bptr, nb, (int32_t*)(ws + L.off_scan), L.nnz > 0 ? bfill : nullptr, st)) != hipSuccess)
+    return e;
   if (L.nnz > 0) {
-    int64_t cblocks = (nb + 255) / 256;
-    if (cblocks > 65536) cblocks = 65536;
-    hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)cblocks), dim3(256), 0, st, bfill, (const int32_t*)bptr, nb);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(runs ? k_bucket_runs<true> : k_bucket<true>, dim3((unsigned)blocks), dim3(256), 0, st,
                        ctl, (const int2*)(ws + L.off_rptr), item_ids, L.V, L.nnz, rows_side, tile, minor, bfill, pairs,
                        (int*)nullptr);
@@ -700,6 +754,8 @@ hipError_t launch_buckets(const Layout& L, char* ws, const int32_t* item_ids, bo
 }
 
 hipError_t launch_no_row_buckets(const Layout& L, char* ws, hipStream_t st) {
+  // the bf16 forward sweeps without Cut Metrics are compiled without positives and read no bucket pointers
+  if (L.dtype == 1) return hipSuccess;
   return launch_fill_i32((int32_t*)(ws + L.off_bptr_r), L.nb_r + 1, 0, st);
 }
 
