@@ -518,7 +518,8 @@ hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp
 // Multi-block exclusive scan of int32 counts, in place: x[i] <- sum_{j<i} x[j] for i <= n (x[n] = total), and
 // optionally the scanned x[0..n) copied to `copy` as well. Thread t of block b owns the 8 entries from
 // b * kScanBlock + 8 t (one 32-byte run: two 16-byte loads and stores where the run lies inside [0, n)); entry n
-// (the grand total) falls in the first run that reaches past n - 1.
+// (the grand total) falls in the first run that reaches past n - 1. Two passes: k_scan_sums leaves each block's
+// total; k_scan_apply adds up the totals of the blocks before its own, then scans its block.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kScanPerThread = kScanBlock / 1024;
 static_assert(kScanPerThread == 8, "two 16-byte vectors per thread");
@@ -547,23 +548,6 @@ __global__ void __launch_bounds__(1024) k_scan_sums(const int32_t* __restrict__ 
   if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
-__global__ void __launch_bounds__(1024) k_scan_bsums(int32_t* bsum, int64_t nb) {
-  __shared__ int sh[16];
-  __shared__ int base;
-  if (threadIdx.x == 0) base = 0;
-  __syncthreads();
-  for (int64_t c0 = 0; c0 < nb; c0 += 1024) {
-    const int64_t i = c0 + threadIdx.x;
-    const int v = i < nb ? bsum[i] : 0;
-    int tot;
-    const int ex = block_excl_scan(v, sh, tot);
-    if (i < nb) bsum[i] = base + ex;
-    __syncthreads();
-    if (threadIdx.x == 0) base += tot;
-    __syncthreads();
-  }
-}
-
 __global__ void __launch_bounds__(1024) k_scan_apply(int32_t* __restrict__ x, int64_t n,
                                                      const int32_t* __restrict__ bsum, int32_t* __restrict__ copy) {
   __shared__ int sh[16];
@@ -573,8 +557,12 @@ __global__ void __launch_bounds__(1024) k_scan_apply(int32_t* __restrict__ x, in
   int s = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += v[j];
-  int tot;
-  int run = block_excl_scan(s, sh, tot) + bsum[blockIdx.x];
+  // the block's base: the sums of the blocks before it (integers: any order gives the same total)
+  int before = 0;
+  for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += 1024) before += bsum[i];
+  int base, tot;
+  (void)block_excl_scan(before, sh, base);
+  int run = block_excl_scan(s, sh, tot) + base;
   int o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -602,7 +590,6 @@ static hipError_t scan_exclusive(int32_t* x, int64_t n, int32_t* tmp, int32_t* c
   // n + 1 entries are written; blocks cover [0, n] inclusive
   const int64_t nb = (n + 1 + kScanBlock - 1) / kScanBlock;
   hipLaunchKernelGGL(k_scan_sums, dim3((unsigned)nb), dim3(1024), 0, st, x, n, tmp);
-  hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(1024), 0, st, tmp, nb);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(1024), 0, st, x, n, (const int32_t*)tmp, copy);
   return hipGetLastError();
 }
