@@ -433,34 +433,34 @@ hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t
 // E preparation: block = kEBlkItems items, processed 32 at a time through LDS. Writes the slot-packed Evp
 // (when requested) and float64 column sums per block.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t V, int D,
-                                                T* __restrict__ Evp, double* __restrict__ sum_part) {
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t V, T* __restrict__ Evp,
+                                                double* __restrict__ sum_part) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
   const int tid = threadIdx.x;
-  const int upr = D * (int)sizeof(T) / 16;
+  constexpr int upr = D * (int)sizeof(T) / 16;  // 16-byte units per row
+  constexpr int kU = 32 * upr / 256;             // units per thread and 32-item chunk (1 ... 8)
+  static_assert(kU >= 1 && 32 * upr % 256 == 0, "whole units per thread");
   double acc0 = 0.0, acc1 = 0.0;  // column sums for d = tid and d = tid + 256
   const int64_t v_begin = (int64_t)blockIdx.x * kEBlkItems;
-  // the 16-byte units of a 32-item chunk, unit u = tid + 256 q (at most 8 per thread: D * sizeof(T) <= 1024);
-  // the next chunk's units are loaded while the current one is packed
-  constexpr int kMaxU = 8;
-  u32x4 nx[kMaxU];
+  // unit u = tid + 256 q of a chunk; the next chunk's units are loaded while the current one is packed
+  u32x4 nx[kU];
   auto load_chunk = [&](int64_t v0) {
 #pragma unroll
-    for (int q = 0; q < kMaxU; ++q) {
+    for (int q = 0; q < kU; ++q) {
       const int u = tid + 256 * q, rr = u / upr, c = u % upr;
       nx[q] = u32x4{0u, 0u, 0u, 0u};
-      if (u < 32 * upr && v0 + rr < V) nx[q] = *(const u32x4*)((const char*)E + ((v0 + rr) * D) * sizeof(T) + c * 16);
+      if (v0 + rr < V) nx[q] = *(const u32x4*)((const char*)E + ((v0 + rr) * D) * sizeof(T) + c * 16);
     }
   };
   load_chunk(v_begin);
   for (int ch = 0; ch < kEBlkItems / 32; ++ch) {
     const int64_t v0 = v_begin + ch * 32;
 #pragma unroll
-    for (int q = 0; q < kMaxU; ++q) {
+    for (int q = 0; q < kU; ++q) {
       const int u = tid + 256 * q, rr = u / upr, c = u % upr;
-      if (u < 32 * upr) *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = nx[q];
+      *(u32x4*)((char*)tile + ((int64_t)rr * D) * sizeof(T) + c * 16) = nx[q];
     }
     __syncthreads();
     if (ch + 1 < kEBlkItems / 32) load_chunk(v0 + 32);
@@ -500,14 +500,28 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
   if (tid + 256 < D) sum_part[blockIdx.x * (int64_t)D + tid + 256] = acc1;
 }
 
+template <typename T, int D>
+static void prep_e_launch(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {
+  hipLaunchKernelGGL((k_prep_e<T, D>), dim3((unsigned)L.n_eblk), dim3(256), (size_t)32 * D * sizeof(T), st,
+                     (const T*)E, L.V, want_evp ? (T*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+}
+
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {
-  const size_t sm = (size_t)32 * L.D * L.esz;
   if (L.dtype == 1) {
-    hipLaunchKernelGGL(k_prep_e<__bf16>, dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const __bf16*)E, L.V,
-                       L.D, want_evp ? (__bf16*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+    switch (L.D) {
+      case 64: prep_e_launch<__bf16, 64>(L, ws, E, want_evp, st); break;
+      case 128: prep_e_launch<__bf16, 128>(L, ws, E, want_evp, st); break;
+      case 256: prep_e_launch<__bf16, 256>(L, ws, E, want_evp, st); break;
+      case 512: prep_e_launch<__bf16, 512>(L, ws, E, want_evp, st); break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
-    hipLaunchKernelGGL(k_prep_e<float>, dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const float*)E, L.V, L.D,
-                       want_evp ? (float*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+    switch (L.D) {
+      case 64: prep_e_launch<float, 64>(L, ws, E, want_evp, st); break;
+      case 128: prep_e_launch<float, 128>(L, ws, E, want_evp, st); break;
+      case 256: prep_e_launch<float, 256>(L, ws, E, want_evp, st); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
