@@ -218,6 +218,46 @@ def test_de_polynomial_and_exact_waves_side_by_side():
     _check(p, _run(p, g=1.25), ref)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_polynomial_and_exact_waves_side_by_side(D):
+    """The forward sweep's waves (bf16, D <= 128) choose their epilogue from the bound max ||H[r]|| over their 32
+    rows times max_v ||E[v]||: the short polynomial up to 0.45, the long one up to 0.8, else the exact form. Here
+    the largest item norm is 1 and groups of 32 valid rows (in compacted order) cycle through norms inside the
+    short form's range, at its edge, at the long form's edge and beyond it; unit items aligned with some rows of
+    the edge groups give |z| close to the bound. One call, positives everywhere, masked rows in between, and the
+    backward's recompute path for dH as well."""
+    R, V = 32 * 24 + 40, 3000
+    p = W.custom_problem(R, V, D, dtype="bf16", seed=81 + D, h_std=1.0, e_std=1.0, pos_per_row=(1, 12),
+                         mask_frac=0.15)
+    valid = torch.nonzero(p["row_mask"].bool()).flatten()
+    H = p["H"].float()
+    H = H / H.norm(dim=1, keepdim=True)
+    E = p["E"].float()
+    E = E / E.norm(dim=1, keepdim=True) * torch.linspace(0.05, 1.0, V).unsqueeze(1)  # largest norm 1
+    norms = torch.tensor([0.3, 0.44, 0.79, 2.5])
+    group = torch.arange(valid.numel()) // 32 % 4
+    H[valid] = H[valid] * norms[group].unsqueeze(1)
+    for gi in (1, 2):
+        edge = valid[group == gi]
+        for j in range(0, edge.numel(), 7):  # unit items along edge rows: z = ||H[r]||
+            E[(97 * j + 31 * gi) % V] = H[edge[j]] / H[edge[j]].norm()
+    p["H"], p["E"] = H.to(torch.bfloat16), E.to(torch.bfloat16)
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.75)
+    _check(p, _run(p, g=0.75), ref)
+    _check(p, _run(p, g=0.75, use_saved=False), ref)
+
+
+@pytest.mark.parametrize("e_scale,D", [(1e-5, 64), (1e-5, 128), (3e3, 128)])
+def test_forward_f16_evp_scaling(e_scale, D):
+    """The f16 slot-packed copy of E used by the forward's gradient GEMM (bf16, D <= 128) is scaled by a power
+    of two chosen from max |E|: tiny E (polynomial waves) and large E (exact waves) must give dH at full
+    accuracy."""
+    p = W.custom_problem(256, 2000, D, dtype="bf16", seed=82, h_std=1.0 / math.sqrt(D), e_std=e_scale,
+                         pos_per_row=(1, 6), mask_frac=0.2)
+    ref = oracle.full(p["H"], p["E"], p["row_offsets"], p["item_ids"], p["row_mask"], g=0.5)
+    _check(p, _run(p, g=0.5), ref, excess=e_scale > 1e-3)
+
+
 @pytest.mark.parametrize("h_scale,D", [(1e-5, 128), (3e3, 128), (1e-5, 512), (3e3, 256)])
 def test_de_f16_operand_scaling(h_scale, D):
     """The f16 copy of the rows used by the dE sweep is scaled by a power of two chosen from max |w H|: tiny and

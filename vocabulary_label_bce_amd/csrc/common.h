@@ -74,6 +74,8 @@ struct Ctl {           // device control block
   double scale;        // s = 1 / (W * V), W = summed weight of the valid rows (R_v without weights); 0 when W == 0
   uint32_t hnorm_max;  // bits of max_r ||H[r]|| over the valid rows (a non-negative float), set by the H preparation
   uint32_t hw_absmax;  // bits of max |w_r H[r][d]| over the valid rows (the f16 gradient operand's scale)
+  uint32_t enorm_max;  // bits of max_v ||E[v]|| (set by the E statistics pass of the f16-Evp shapes)
+  uint32_t e_absmax;   // bits of max |E[v][d]| (the f16 slot-packed E copy's scale; same pass)
 };
 
 // Shapes whose dE sweep runs its gradient GEMM in f16 (every bf16 input): the slot-packed rows Hrp are stored as
@@ -86,6 +88,12 @@ __host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return 
 // and holds D[m = 4(l/16) + i][n = l%16], i < 4). Its slot-packed copies (Evp, Hrp) of a 32-row block X use:
 // for 16-wide d-block db and lane l, the 8 elements X[sp16_row(l, j)][16 db + l % 16] (j = 0..7) stored together.
 __host__ __device__ constexpr inline bool narrow_owner(int dtype, int D) { return dtype == 1 && D >= 256; }
+
+// Shapes whose forward sweep runs its gradient GEMM in f16 (bf16 input on the 32-owner engines, D <= 128): the
+// slot-packed E copy Evp is stored as f16 scaled by 2^hrp_shift(e_absmax), the G tiles are f16, and the dH
+// partials are multiplied by 2^-shift when written. The E statistics pass (max ||E[v]||, max |E|) runs first;
+// the row norm bound also lets the forward sweep take its polynomial epilogue.
+__host__ __device__ constexpr inline bool evp_is_f16(int dtype, int D) { return dtype == 1 && D <= 128; }
 __host__ __device__ constexpr inline int sp16_row(int lane, int j) { return 16 * (j / 4) + 4 * (lane / 16) + (j % 4); }
 __host__ __device__ constexpr inline int64_t sp16_off(int db, int lane) { return ((int64_t)db * 64 + lane) * 8; }
 
@@ -112,6 +120,7 @@ struct Layout {
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
   size_t off_sumE, off_sumE_part, off_sum2, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
+  size_t off_estat;  // per-block maxima of the E statistics pass
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan, off_cpart;
   size_t scan_elems;
   int64_t part_rows;  // rows of the forward sweep's unit-major partial buffers

@@ -156,6 +156,8 @@ __global__ void __launch_bounds__(1024) k_compact_scatter(const uint8_t* __restr
     ctl->bad_ids = 0;
     ctl->hnorm_max = 0u;
     ctl->hw_absmax = 0u;
+    ctl->enorm_max = 0u;
+    ctl->e_absmax = 0u;
     ctl->scale = W != 0.0 ? 1.0 / (W * (double)V) : 0.0;
   }
 }
@@ -187,6 +189,14 @@ __device__ inline void set_run<__bf16>(bf16x8& run, const __bf16* tile, int D, i
 template <>
 __device__ inline void set_run<float>(float& run, const float* tile, int D, int db, int g, int lane) {
   run = tile[acc_pos(g, lane / 32) * D + db * 32 + lane % 32];
+}
+
+// The bf16 run as f16 scaled by 2^sh (an exact power of two): the 8 significant bits of each value are kept
+// exactly wherever the scaled value is a normal f16 (every value within 2^29 of the largest, which the scale
+// brings into [2^14, 2^15)).
+__device__ inline void set_run_f16(f16x8& run, const __bf16* tile, int D, int db, int g, int lane, float sc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) run[j] = (_Float16)((float)tile[acc_pos(g * 8 + j, lane / 32) * D + db * 32 + lane % 32] * sc);
 }
 
 // The same run with each value times its row's weight w[row] (a weight of 1 leaves it unchanged; others round
@@ -430,12 +440,90 @@ hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// E statistics (bf16, D <= 128): max_v ||E[v]|| and max |E[v][d]|. One item per group of D/8 lanes, one 16-byte
+// load per lane, grid-stride over the items; each block writes its two maxima to part[2 b], part[2 b + 1], and
+// k_stats_e_final folds them into the control block (no contended atomics: one per block on a single address
+// measured about 80 us at 2,048 blocks). A NaN anywhere makes the results NaN, which no bound test passes.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kStatBlocks = 2048;  // most blocks of the E statistics pass
+
+template <int D>
+__global__ void __launch_bounds__(256) k_stats_e(const __bf16* __restrict__ E, int64_t V, float* __restrict__ part) {
+  constexpr int LPI = D / 8;          // lanes per item
+  constexpr int IPB = 256 / LPI;      // items per block and pass
+  __shared__ float sh_n[4], sh_a[4];
+  const int tid = threadIdx.x, sub = tid % LPI;
+  float nmax = 0.f, amax = 0.f;
+  for (int64_t v = (int64_t)blockIdx.x * IPB + tid / LPI; v - tid / LPI < V; v += (int64_t)gridDim.x * IPB) {
+    float n2 = 0.f;
+    if (v < V) {
+      const bf16x8 x = *(const bf16x8*)(E + v * D + sub * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = (float)x[j];
+        n2 += f * f;
+        amax = fmaxf(amax, __builtin_fabsf(f));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPI; o <<= 1) n2 += __shfl_xor(n2, o, 64);
+    nmax = fmaxf(nmax, n2);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    nmax = fmaxf(nmax, __shfl_xor(nmax, o, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  }
+  if (tid % 64 == 0) {
+    sh_n[tid / 64] = nmax;
+    sh_a[tid / 64] = amax;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    part[2 * blockIdx.x] = sqrtf(fmaxf(fmaxf(sh_n[0], sh_n[1]), fmaxf(sh_n[2], sh_n[3])));
+    part[2 * blockIdx.x + 1] = fmaxf(fmaxf(sh_a[0], sh_a[1]), fmaxf(sh_a[2], sh_a[3]));
+  }
+}
+
+// One block: the largest of the blocks' maxima (NaN-propagating, so a NaN partial makes the result NaN).
+__global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict__ part, int nblk, Ctl* __restrict__ ctl) {
+  __shared__ float sh[2][16];
+  const int tid = threadIdx.x;
+  float n = 0.f, a = 0.f;
+  for (int b = tid; b < nblk; b += 1024) {
+    const float pn = part[2 * b], pa = part[2 * b + 1];
+    n = (pn > n || pn != pn) ? pn : n;
+    a = (pa > a || pa != pa) ? pa : a;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float on = __shfl_xor(n, o, 64), oa = __shfl_xor(a, o, 64);
+    n = (on > n || on != on) ? on : n;
+    a = (oa > a || oa != oa) ? oa : a;
+  }
+  if (tid % 64 == 0) {
+    sh[0][tid / 64] = n;
+    sh[1][tid / 64] = a;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 16; ++w) {
+      n = (sh[0][w] > n || sh[0][w] != sh[0][w]) ? sh[0][w] : n;
+      a = (sh[1][w] > a || sh[1][w] != sh[1][w]) ? sh[1][w] : a;
+    }
+    ctl->enorm_max = __float_as_uint(n);
+    ctl->e_absmax = __float_as_uint(a);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // E preparation: block = kEBlkItems items, processed 32 at a time through LDS. Writes the slot-packed Evp
-// (when requested) and float64 column sums per block.
+// (when requested; f16 scaled by 2^hrp_shift(e_absmax) for the evp_is_f16 shapes) and float64 column sums per
+// block.
 // ---------------------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t V, T* __restrict__ Evp,
-                                                double* __restrict__ sum_part) {
+                                                double* __restrict__ sum_part, const Ctl* __restrict__ ctl) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
   const int tid = threadIdx.x;
@@ -479,6 +567,19 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
         packed = true;
       }
     }
+    if constexpr (sizeof(T) == 2 && evp_is_f16(1, D)) {
+      if (Evp) {
+        _Float16* dst = (_Float16*)(Evp + v0 * D);
+        const float sc = ldexpf(1.f, hrp_shift(ctl->e_absmax));
+        for (int q = tid; q < (D / 32) * 2 * 64; q += 256) {
+          const int lane = q % 64, g = (q / 64) % 2, db = q / 128;
+          f16x8 run;
+          set_run_f16(run, tile, D, db, g, lane, sc);
+          *(f16x8*)(dst + slot_off<T>(D, db, g, lane)) = run;
+        }
+        packed = true;
+      }
+    }
     if (Evp && !packed) {
       T* dst = Evp + v0 * D;
       const int runs = (D / 32) * Elem<T>::kGroups * 64;
@@ -502,8 +603,19 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
 
 template <typename T, int D>
 static void prep_e_launch(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {
+  Ctl* ctl = (Ctl*)(ws + L.off_ctl);
+  if constexpr (sizeof(T) == 2 && evp_is_f16(1, D)) {
+    if (want_evp) {
+      const int64_t need = (L.V + 256 / (D / 8) - 1) / (256 / (D / 8));
+      const int blocks = (int)(need < kStatBlocks ? need : kStatBlocks);
+      float* part = (float*)(ws + L.off_estat);
+      hipLaunchKernelGGL((k_stats_e<D>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)E, L.V, part);
+      hipLaunchKernelGGL(k_stats_e_final, dim3(1), dim3(1024), 0, st, (const float*)part, blocks, ctl);
+    }
+  }
   hipLaunchKernelGGL((k_prep_e<T, D>), dim3((unsigned)L.n_eblk), dim3(256), (size_t)32 * D * sizeof(T), st,
-                     (const T*)E, L.V, want_evp ? (T*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part));
+                     (const T*)E, L.V, want_evp ? (T*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part),
+                     (const Ctl*)ctl);
 }
 
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {

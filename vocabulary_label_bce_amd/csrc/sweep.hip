@@ -357,7 +357,7 @@ template <typename T, int D, int NW, bool FWD, bool GRAD, bool MET = false, int 
           int NDBE = D / 32, bool LOSS = true, bool F16G = false>
 struct Engine {
   using EL = Elem<T>;
-  static_assert(!F16G || (std::is_same<T, __bf16>::value && !FWD && GRAD), "f16 G tiles: the bf16 dE sweep");
+  static_assert(!F16G || (std::is_same<T, __bf16>::value && GRAD), "f16 G tiles: bf16 sweeps with a gradient GEMM");
   using GP = typename std::conditional<F16G, GPackF16, GPack<T>>::type;
   using G = Geo<T, D, NW, GRAD>;
   static constexpr int KS = D / EL::kK, NDB = D / 32;
@@ -866,6 +866,117 @@ struct EpiPoly {
 };
 
 // ---------------------------------------------------------------------------------------------------------
+// Polynomial epilogue of the forward sweep for waves whose logits all satisfy |z| <= B (the sweep checks
+// max_r ||H[r]|| over the wave's rows times max_v ||E[v]||, a Cauchy-Schwarz bound). Per logit it needs the loss
+// term of the signed form, log(1 + e^-z) - ln 2 = -z/2 + log cosh(z/2), and c = sigma(z) - 1/2 = tanh(z/2)/2:
+//   log cosh(z/2) = u/8 - u^2/192 + u^3/2880 - 17 u^4/645120 + ...   (u = z^2),
+//   tanh(z/2)/2   = z (1/4 - u/48 + u^2/480 - 17 u^3/80640 + 31 u^4/1451520 - ...).
+// Both are alternating series with decreasing terms for |z| <= 1, so the error is below the first omitted term.
+// Long form (B = 0.8): loss through u^3, c through u^3: errors below 4.4e-6 per loss term (1.4e-5 of the smallest
+// possible BCE term, softplus(-1) > 0.31) and 2.9e-6 on c. Short form (B = 0.45): loss through u^2, c through
+// u^2: errors below 3.2e-6 per loss term and 3.2e-6 on c, two operations less per pair of logits. The arithmetic
+// runs on packed f16 pairs (z rounded once to f16, relative 2^-11); the loss terms are summed in fp32 by
+// v_dot2_f32_f16 (exact f16 products), and c is written straight into the f16 G tile.
+// ---------------------------------------------------------------------------------------------------------
+constexpr float kPolyBoundF = 0.8f;       // long form
+constexpr float kPolyBoundShort = 0.45f;  // short form
+struct PolyStateF {
+  f16x2 zh[8], u[8], t[8], l[8];
+  float e;  // the step's loss terms, summed
+};
+
+template <int NSLOT, bool SHORT>
+struct EpiPolyF {
+  enum { kCz = 1, kZ2, kP3, kP2, kP1, kC, kL2, kL1, kLa, kLz };
+  struct Tbl {
+    short op[80];
+    short start[34];
+    int n;
+  };
+  // pairs of logit pairs through every stage, so a pair's operations are spread over a few MFMA slots
+  static constexpr Tbl make() {
+    Tbl t{};
+    int n = 0;
+    auto push = [&](int kind, int arg) { t.op[n++] = (short)(kind * 64 + arg); };
+    for (int p = 0; p < 8; p += 2)
+      for (int kind = kCz; kind <= kLz; ++kind) {
+        if (SHORT && (kind == kP3 || kind == kL2)) continue;
+        push(kind, p);
+        push(kind, p + 1);
+      }
+    t.n = n;
+    for (int j = 0; j <= NSLOT; ++j) t.start[j] = (short)(n * j / (NSLOT > 0 ? NSLOT : 1));
+    return t;
+  }
+  static constexpr Tbl tbl = make();
+  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+
+  // Each result is tied to an empty asm statement where it is computed: otherwise the optimiser moves this pure
+  // arithmetic out of its MFMA slot (measured: the loss sums of all six unrolled iterations sunk into the last
+  // one, other stages hoisted in front of the first MFMA), which leaves the MFMAs without vector work beside them.
+  template <typename X>
+  __device__ static inline void pin(X& x) {
+    asm volatile("" : "+v"(x));
+  }
+  template <int OPC>
+  __device__ static inline void op(const f32x16& z, PolyStateF& s, f16x8* gn) {
+    constexpr int kind = OPC / 64, a = OPC % 64;
+    const f16x2 c3 = {(_Float16)(-17.0 / 80640.0), (_Float16)(-17.0 / 80640.0)};
+    const f16x2 c2 = {(_Float16)(1.0 / 480.0), (_Float16)(1.0 / 480.0)};
+    const f16x2 c1 = {(_Float16)(-1.0 / 48.0), (_Float16)(-1.0 / 48.0)};
+    const f16x2 c0 = {(_Float16)0.25, (_Float16)0.25};
+    const f16x2 b3 = {(_Float16)(1.0 / 2880.0), (_Float16)(1.0 / 2880.0)};
+    const f16x2 b2 = {(_Float16)(-1.0 / 192.0), (_Float16)(-1.0 / 192.0)};
+    const f16x2 b1 = {(_Float16)0.125, (_Float16)0.125};
+    if constexpr (kind == kCz) {
+      s.zh[a] = f16x2{(_Float16)z[2 * a], (_Float16)z[2 * a + 1]};
+      pin(s.zh[a]);
+    } else if constexpr (kind == kZ2) {
+      s.u[a] = s.zh[a] * s.zh[a];
+      pin(s.u[a]);
+    } else if constexpr (kind == kP3) {
+      s.t[a] = s.u[a] * c3 + c2;
+      pin(s.t[a]);
+    } else if constexpr (kind == kP2) {
+      s.t[a] = s.u[a] * (SHORT ? c2 : s.t[a]) + c1;
+      pin(s.t[a]);
+    } else if constexpr (kind == kP1) {
+      s.t[a] = s.u[a] * s.t[a] + c0;
+      pin(s.t[a]);
+    } else if constexpr (kind == kC) {
+      f16x2 c = s.zh[a] * s.t[a];
+      pin(c);
+      gn[a / 4][2 * (a % 4)] = c[0];
+      gn[a / 4][2 * (a % 4) + 1] = c[1];
+    } else if constexpr (kind == kL2) {
+      s.l[a] = s.u[a] * b3 + b2;
+      pin(s.l[a]);
+    } else if constexpr (kind == kL1) {
+      s.l[a] = s.u[a] * (SHORT ? b2 : s.l[a]) + b1;
+      pin(s.l[a]);
+    } else if constexpr (kind == kLa) {  // + u (1/8 - u/192 + u^2/2880) for both logits
+      s.e = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.l[a]), __builtin_bit_cast(h2, s.u[a]), s.e, false);
+      pin(s.e);
+    } else if constexpr (kind == kLz) {  // - z/2 for both logits
+      s.e = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.zh[a]), (h2){-0.5, -0.5}, s.e, false);
+      pin(s.e);
+    }
+  }
+  template <int I, int E>
+  __device__ static inline void ops(const f32x16& z, PolyStateF& s, f16x8* gn) {
+    if constexpr (I < E) {
+      op<tbl.op[I]>(z, s, gn);
+      ops<I + 1, E>(z, s, gn);
+    }
+  }
+  template <int J>
+  __device__ static inline void slot(const f32x16& z, PolyStateF& s, f16x8* gn) {
+    ops<tbl.start[J], tbl.start[J + 1]>(z, s, gn);
+  }
+  __device__ static inline void all(const f32x16& z, PolyStateF& s, f16x8* gn) { ops<0, tbl.n>(z, s, gn); }
+};
+
+// ---------------------------------------------------------------------------------------------------------
 // Interleaved step engine for bf16 operands with D <= 128 (8 waves per workgroup, two per SIMD).
 //
 // With two waves per SIMD the matrix pipe accepts MFMAs from both, so the sweep runs at the MFMA rate only if
@@ -1062,24 +1173,27 @@ struct Pipe {
   }
   // Slot J: MFMA J, its share of the epilogue, and the LDS read of the operand of MFMA J + RA. sched_barrier
   // keeps the slots in order (the compiler would otherwise issue each read right before its MFMA).
-  // POLY: the polynomial epilogue (writes the next G tile gn; the gradient MFMAs use the carried g) instead of
+  // POLY 1 / 2: the polynomial epilogue (2: the forward's short form; writes the next G tile gn; the gradient
+  // MFMAs use the carried g) instead of
   // the exact one (packs the carried c of the previous step into st.g for the gradient MFMAs, writes the new c).
-  template <int J, bool POLY>
+  template <int J, int POLY>
   __device__ inline void slots(int sAr, int sBr, const bf16x8* own, f32x16* acc, f32x16& zn, const f32x16& zc,
-                               float* c, typename ES::State& st, PolyState& ps, const GOp* g, GOp* gn,
-                               bf16x8* opnd) const {
+                               float* c, typename ES::State& st, PolyState& ps, PolyStateF& psf, const GOp* g,
+                               GOp* gn, bf16x8* opnd) const {
     if constexpr (J < NM) {
       if constexpr (GRAD && (J & 1))
         acc[J >> 2] = mma_g((POLY ? g : st.g)[(J >> 1) & 1], __builtin_bit_cast(GOp, opnd[J]), acc[J >> 2]);
       else
         zn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[J], own[GRAD ? J >> 1 : J], zn, 0, 0, 0);
-      if constexpr (POLY)
+      if constexpr (POLY && FWD)
+        EpiPolyF<NM, POLY == 2>::template slot<J>(zc, psf, gn);
+      else if constexpr (POLY)
         EpiPoly<NM>::template slot<J>(zc, ps, gn);
       else
         ES::template slot<J>(zc, c, st);
       if constexpr (J + RA < NM) opnd[J + RA] = opnd_read(J + RA, sAr, sBr);
       __builtin_amdgcn_sched_barrier(0);
-      slots<J + 1, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, g, gn, opnd);
+      slots<J + 1, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, psf, g, gn, opnd);
     }
   }
 
@@ -1099,11 +1213,12 @@ struct Pipe {
 
   // The previous step's G tile is carried in c (exact epilogue: float values, packed inside the iteration) or in
   // g (polynomial epilogue: packed f16); on return they hold step i's.
-  // POLY (dE sweep with F16G only): the polynomial epilogue.
-  template <bool HASG, bool POLY>
+  // POLY (F16G sweeps): the polynomial epilogue (EpiPoly in the dE sweep, EpiPolyF in the forward).
+  template <bool HASG, int POLY>
   __device__ inline void iter(int i, int sAr, int sBr, int sAw, int sBw, bool bar, const bf16x8* own,
                               f32x16* acc, f32x16& zc, float* c, GOp* g, float& e_acc, float& posz) {
-    static_assert(!POLY || (F16G && !FWD && GRAD), "polynomial epilogue: f16 dE sweep only");
+    static_assert(!POLY || (F16G && GRAD && !(FWD && POS)), "polynomial epilogue: f16 sweeps (forward: gathered positives)");
+    static_assert(POLY != 2 || FWD, "short polynomial: forward only");
     const bool newblk = bar && (i & 63) == 0;
     if (bar) {
       wait_vm_and_barrier<INFL>();
@@ -1113,6 +1228,8 @@ struct Pipe {
     if (newblk) bkt_dma((i >> 6) + 1);  // after the ring loads: the next barrier waits for nothing extra
     typename ES::State st;
     PolyState ps;
+    PolyStateF psf;
+    psf.e = 0.f;
     GOp gn[2];
     f32x16 zn;
     if constexpr (HASG || !GRAD) {
@@ -1122,15 +1239,18 @@ struct Pipe {
       if constexpr (!POLY) ES::pre(zc, c, st);
       zn = f32x16{};
       __builtin_amdgcn_sched_barrier(0);
-      slots<0, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, g, gn, opnd);
+      slots<0, POLY>(sAr, sBr, own, acc, zn, zc, c, st, ps, psf, g, gn, opnd);
     } else {
       zn = logits(sAr, own);
-      if constexpr (POLY)
+      if constexpr (POLY && FWD)
+        EpiPolyF<NM, POLY == 2>::all(zc, psf, gn);
+      else if constexpr (POLY)
         EpiPoly<NM>::all(zc, ps, gn);
       else
         ES::all(zc, c, st);
     }
     if constexpr (POLY) {
+      if (FWD) e_acc += psf.e;
       if (POS && __builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
       g[0] = gn[0];
       g[1] = gn[1];
@@ -1150,7 +1270,7 @@ struct Pipe {
   }
 
   // Runs the steps [j0, j1) of a unit. own: owner operand; acc: gradient tiles; e_acc / posz: forward row sums.
-  template <bool POLY = false>
+  template <int POLY = 0>
   __device__ inline void run(const bf16x8* own, f32x16* acc, float& e_acc, float& posz) {
     const int n = j1 - j0;
     if (n <= 0) return;
@@ -1171,10 +1291,15 @@ struct Pipe {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     block_start(0);
     f32x16 zc = logits(0, own);
+    // Step 0's A slot is refilled (step NR) by the loads of iteration 1, and neither iteration 0 nor 1 opens a
+    // barrier: every wave's reads of it must be done before any wave gets there. Without this barrier a wave
+    // that ran an iteration ahead (measured: on a kernel's first, cold launch) overwrote the block under a
+    // wave still reading it, changing a few logits of that wave's rows.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float c[16];  // G tile of the last epilogue (exact epilogue)
     GOp g[2];     // the same, packed (polynomial epilogue)
-    // iteration 0: logits of step 1, epilogue of step 0 (no gradient yet); it counts as a barrier iteration
-    // (the one before the loop)
+    // iteration 0: logits of step 1, epilogue of step 0 (no gradient yet); with the barrier above it counts
+    // as a barrier iteration (the one before the loop)
     iter<false, POLY>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, g, e_acc, posz);
     int i = 1;
     // iterations 1 + 6m + u: slots A read (2 + u) % 6, B read u, A load u, B load (4 + u) % 6; barrier at odd u
@@ -1241,7 +1366,10 @@ template <typename T, int D, int NW, bool WITH_DH, bool MET, int KT, int DHPART 
 __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   using EL = Elem<T>;
   constexpr int NDB = D / 32, NDBE = DHPART ? NDB / 2 : NDB, DB0 = DHPART == 2 ? NDB / 2 : 0;
-  using EN = Engine<T, D, NW, true, WITH_DH, MET, KT, DB0, NDBE, DHPART != 2>;
+  // bf16, D <= 128: the gradient GEMM takes f16 G tiles and the f16 Evp (scaled by 2^s; dH partials unscaled
+  // when written)
+  constexpr bool kF16 = std::is_same<T, __bf16>::value && evp_is_f16(1, D) && WITH_DH;
+  using EN = Engine<T, D, NW, true, WITH_DH, MET, KT, DB0, NDBE, DHPART != 2, kF16>;
   constexpr int RW = NW * 32, KS = D / EL::kK;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
@@ -1259,7 +1387,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
   const int start = (int)(((int64_t)x * U) / 8), cnt = (int)(((int64_t)(x + 1) * U) / 8) - start;
 
   constexpr bool kPipe = use_pipe<T, D, NW, MET, KT, DHPART>();
-  using PP = Pipe<D <= 128 ? D : 128, true, WITH_DH>;
+  using PP = Pipe<D <= 128 ? D : 128, true, WITH_DH, kF16>;
   EN en;
   PP pp;
   if constexpr (kPipe) {
@@ -1310,9 +1438,31 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     TopK<KT ? KT : 1> tk;
     if (KT) tk.init();
 
-    if constexpr (kPipe)
+    if constexpr (kPipe && kF16) {
+      // |z| <= ||H[r]|| ||E[v]|| <= kPolyBoundF (kPolyBoundShort) for every logit of this wave: the polynomial
+      // epilogue (its short form) applies
+      float n2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (float)((const bf16x8*)hop)[ks][j];
+          n2 += x * x;
+        }
+      n2 += __shfl_xor(n2, 32, 64);  // the two halves of the row
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
+      const float bound = sqrtf(n2) * __uint_as_float(a.ctl->enorm_max);
+      const int form = __builtin_amdgcn_readfirstlane(bound <= kPolyBoundShort ? 2 : (bound <= kPolyBoundF ? 1 : 0));
+      if (form == 2)
+        pp.template run<2>((const bf16x8*)hop, acc, e_acc, posz);
+      else if (form == 1)
+        pp.template run<1>((const bf16x8*)hop, acc, e_acc, posz);
+      else
+        pp.template run<0>((const bf16x8*)hop, acc, e_acc, posz);
+    } else if constexpr (kPipe) {
       pp.run((const bf16x8*)hop, acc, e_acc, posz);
-    else
+    } else
       en.run(hop, acc, e_acc, posz, met, &tk);
 
     // unit results: per-row loss parts and the dH partial of this split
@@ -1349,11 +1499,12 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
       if (lane < 32) a.metpart[urow + lane] = make_int4(met[0], met[1], met[2], 0);
     }
     if (WITH_DH) {
+      const float unscale = kF16 ? ldexpf(1.f, -hrp_shift(a.ctl->e_absmax)) : 1.f;
 #pragma unroll
       for (int db = 0; db < NDBE; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          a.dhpart[(urow + acc_pos(i, lane / 32)) * D + (DB0 + db) * 32 + lane % 32] = acc[db][i];
+          a.dhpart[(urow + acc_pos(i, lane / 32)) * D + (DB0 + db) * 32 + lane % 32] = acc[db][i] * unscale;
     }
   }
 }
@@ -1445,9 +1596,9 @@ __global__ void __launch_bounds__(NW * 64) k_items(ItemsArgs a) {
     for (int o = 1; o < 32; o <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
     const float bound = sqrtf(n2) * __uint_as_float(a.ctl->hnorm_max);
     if (__builtin_amdgcn_readfirstlane(bound <= kPolyBound ? 1 : 0))
-      pp.template run<true>((const bf16x8*)eop, acc, e_acc, posz);
+      pp.template run<1>((const bf16x8*)eop, acc, e_acc, posz);
     else
-      pp.template run<false>((const bf16x8*)eop, acc, e_acc, posz);
+      pp.template run<0>((const bf16x8*)eop, acc, e_acc, posz);
   } else if (n_st > 0) {
     EN en;
     en.setup(lds, wave, lane);
