@@ -443,7 +443,8 @@ hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t
 // E statistics (bf16, D <= 128): max_v ||E[v]|| and max |E[v][d]|. One item per group of D/8 lanes, one 16-byte
 // load per lane, grid-stride over the items; each block writes its two maxima to part[2 b], part[2 b + 1], and
 // k_stats_e_final folds them into the control block (no contended atomics: one per block on a single address
-// measured about 80 us at 2,048 blocks). A NaN anywhere makes the results NaN, which no bound test passes.
+// measured about 80 us at 2,048 blocks). NaNs do not enter the maxima (fmaxf); a NaN in E gives NaN logits, and
+// so NaN outputs, on either forward epilogue.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kStatBlocks = 2048;  // most blocks of the E statistics pass
 
@@ -452,22 +453,30 @@ __global__ void __launch_bounds__(256) k_stats_e(const __bf16* __restrict__ E, i
   constexpr int LPI = D / 8;          // lanes per item
   constexpr int IPB = 256 / LPI;      // items per block and pass
   __shared__ float sh_n[4], sh_a[4];
+  constexpr int U = 4;                // items per lane group and pass, loaded before any is reduced
   const int tid = threadIdx.x, sub = tid % LPI;
+  const int64_t stride = (int64_t)gridDim.x * IPB;
   float nmax = 0.f, amax = 0.f;
-  for (int64_t v = (int64_t)blockIdx.x * IPB + tid / LPI; v - tid / LPI < V; v += (int64_t)gridDim.x * IPB) {
-    float n2 = 0.f;
-    if (v < V) {
-      const bf16x8 x = *(const bf16x8*)(E + v * D + sub * 8);
+  for (int64_t v0 = (int64_t)blockIdx.x * IPB; v0 < V; v0 += U * stride) {  // block-uniform trip count
+    bf16x8 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * stride + tid / LPI;
+      x[u] = v < V ? *(const bf16x8*)(E + v * D + sub * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float n2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float f = (float)x[j];
+        const float f = (float)x[u][j];
         n2 += f * f;
         amax = fmaxf(amax, __builtin_fabsf(f));
       }
-    }
 #pragma unroll
-    for (int o = 1; o < LPI; o <<= 1) n2 += __shfl_xor(n2, o, 64);
-    nmax = fmaxf(nmax, n2);
+      for (int o = 1; o < LPI; o <<= 1) n2 += __shfl_xor(n2, o, 64);
+      nmax = fmaxf(nmax, n2);
+    }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -485,21 +494,19 @@ __global__ void __launch_bounds__(256) k_stats_e(const __bf16* __restrict__ E, i
   }
 }
 
-// One block: the largest of the blocks' maxima (NaN-propagating, so a NaN partial makes the result NaN).
+// One block: the largest of the blocks' maxima.
 __global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict__ part, int nblk, Ctl* __restrict__ ctl) {
   __shared__ float sh[2][16];
   const int tid = threadIdx.x;
   float n = 0.f, a = 0.f;
   for (int b = tid; b < nblk; b += 1024) {
-    const float pn = part[2 * b], pa = part[2 * b + 1];
-    n = (pn > n || pn != pn) ? pn : n;
-    a = (pa > a || pa != pa) ? pa : a;
+    n = fmaxf(n, part[2 * b]);
+    a = fmaxf(a, part[2 * b + 1]);
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const float on = __shfl_xor(n, o, 64), oa = __shfl_xor(a, o, 64);
-    n = (on > n || on != on) ? on : n;
-    a = (oa > a || oa != oa) ? oa : a;
+    n = fmaxf(n, __shfl_xor(n, o, 64));
+    a = fmaxf(a, __shfl_xor(a, o, 64));
   }
   if (tid % 64 == 0) {
     sh[0][tid / 64] = n;
@@ -508,8 +515,8 @@ __global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict_
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < 16; ++w) {
-      n = (sh[0][w] > n || sh[0][w] != sh[0][w]) ? sh[0][w] : n;
-      a = (sh[1][w] > a || sh[1][w] != sh[1][w]) ? sh[1][w] : a;
+      n = fmaxf(n, sh[0][w]);
+      a = fmaxf(a, sh[1][w]);
     }
     ctl->enorm_max = __float_as_uint(n);
     ctl->e_absmax = __float_as_uint(a);
