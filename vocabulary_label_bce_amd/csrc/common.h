@@ -121,6 +121,7 @@ struct Layout {
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
   size_t off_sumE, off_sumE_part, off_sum2, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
   size_t off_estat;  // per-block maxima of the E statistics pass
+  size_t off_rowform;  // per compacted row: 1 if the forward's waves took the polynomial epilogue (bf16, D <= 128)
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan, off_cpart;
   size_t scan_elems;
   int64_t part_rows;  // rows of the forward sweep's unit-major partial buffers

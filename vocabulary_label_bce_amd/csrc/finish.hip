@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
                                                      int RW, float* __restrict__ row_loss,
                                                      double* __restrict__ rowloss_c, float* __restrict__ dh_out,
                                                      int32_t* __restrict__ metrics, const int2* __restrict__ rptr,
-                                                     const int32_t* __restrict__ ids, const T* __restrict__ E) {
+                                                     const int32_t* __restrict__ ids, const T* __restrict__ E,
+                                                     const uint8_t* __restrict__ rowform) {
   __shared__ float sh_pos[4][512];  // per wave: the positive groups' partial sums (at most 512 floats)
   const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = lane_id();
@@ -190,7 +191,10 @@ __global__ void __launch_bounds__(256) k_rows_finish(const Ctl* __restrict__ ctl
     const int fp = np - tp, fn = npos - tp, tn = (int)(V - tp - fp - fn);
     if (lane < 4) metrics[r * 4 + lane] = lane == 0 ? tp : lane == 1 ? fp : lane == 2 ? fn : tn;
   }
-  const double rl = (double)V * 0.69314718055994530942 + zs + e - p;
+  // rows whose forward waves took the polynomial epilogue summed log cosh(z/2) only: their -z/2 terms, summed over
+  // every item and split, are the rank-1 -H[r].sum_v E[v] / 2
+  const bool poly = rowform && rowform[k];
+  const double rl = (double)V * 0.69314718055994530942 + (poly ? 0.5 * zs : zs) + e - p;
   if (lane == 0) {
     if (row_loss) row_loss[r] = (float)rl;
     rowloss_c[k] = w * rl;
@@ -226,7 +230,7 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
                        (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics, rptr, item_ids,
-                       (const __bf16*)E);
+                       (const __bf16*)E, evp_is_f16(L.dtype, L.D) ? (const uint8_t*)(ws + L.off_rowform) : nullptr);
   } else {
     hipLaunchKernelGGL(k_rows_finish<float>, dim3(blocks), dim3(256), 0, st, ctl, (const float*)H, mask,
                        (const int32_t*)(ws + L.off_compact_of), (const float*)(ws + L.off_wc),
@@ -234,7 +238,7 @@ hipError_t launch_rows_finish(const Layout& L, char* ws, const void* H, const ui
                        (const float2*)(ws + L.off_rowpart), (const int4*)(ws + L.off_metpart),
                        (const double*)(ws + L.off_sumE), L.R, L.V, L.D, L.rows_per_wg, row_loss,
                        (double*)(ws + L.off_rowloss), with_dh ? dh_out : nullptr, metrics, rptr, item_ids,
-                       (const float*)E);
+                       (const float*)E, evp_is_f16(L.dtype, L.D) ? (const uint8_t*)(ws + L.off_rowform) : nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;

@@ -875,19 +875,22 @@ struct EpiPoly {
 // Long form (B = 0.8): loss through u^3, c through u^3: errors below 4.4e-6 per loss term (1.4e-5 of the smallest
 // possible BCE term, softplus(-1) > 0.31) and 2.9e-6 on c. Short form (B = 0.45): loss through u^2, c through
 // u^2: errors below 3.2e-6 per loss term and 3.2e-6 on c, two operations less per pair of logits. The arithmetic
-// runs on packed f16 pairs (z rounded once to f16, relative 2^-11); the loss terms are summed in fp32 by
-// v_dot2_f32_f16 (exact f16 products), and c is written straight into the f16 G tile.
+// runs on packed f16 pairs (z rounded once to f16, relative 2^-11); the log cosh terms are summed in fp32 by
+// v_dot2_f32_f16 (exact f16 products) into two accumulators (even and odd pairs: two dependent chains of four
+// instead of one of eight), and c is written straight into the f16 G tile. The -z/2 terms are not summed here:
+// over a row's items they add up to the rank-1 -H[r].sum_v E[v] / 2, which the finish adds in float64 for the
+// rows flagged as polynomial (a third dot product per pair in the chain cost the sweep 5%).
 // ---------------------------------------------------------------------------------------------------------
 constexpr float kPolyBoundF = 0.8f;       // long form
 constexpr float kPolyBoundShort = 0.45f;  // short form
 struct PolyStateF {
   f16x2 zh[8], u[8], t[8], l[8];
-  float e;  // the step's loss terms, summed
+  float e[2];  // the step's log cosh terms, summed over the even and the odd pairs
 };
 
 template <int NSLOT, bool SHORT>
 struct EpiPolyF {
-  enum { kCz = 1, kZ2, kP3, kP2, kP1, kC, kL2, kL1, kLa, kLz };
+  enum { kCz = 1, kZ2, kP3, kP2, kP1, kC, kL2, kL1, kLa };
   struct Tbl {
     short op[80];
     short start[34];
@@ -899,7 +902,7 @@ struct EpiPolyF {
     int n = 0;
     auto push = [&](int kind, int arg) { t.op[n++] = (short)(kind * 64 + arg); };
     for (int p = 0; p < 8; p += 2)
-      for (int kind = kCz; kind <= kLz; ++kind) {
+      for (int kind = kCz; kind <= kLa; ++kind) {
         if (SHORT && (kind == kP3 || kind == kL2)) continue;
         push(kind, p);
         push(kind, p + 1);
@@ -955,11 +958,8 @@ struct EpiPolyF {
       s.l[a] = s.u[a] * (SHORT ? b2 : s.l[a]) + b1;
       pin(s.l[a]);
     } else if constexpr (kind == kLa) {  // + u (1/8 - u/192 + u^2/2880) for both logits
-      s.e = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.l[a]), __builtin_bit_cast(h2, s.u[a]), s.e, false);
-      pin(s.e);
-    } else if constexpr (kind == kLz) {  // - z/2 for both logits
-      s.e = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.zh[a]), (h2){-0.5, -0.5}, s.e, false);
-      pin(s.e);
+      s.e[a & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.l[a]), __builtin_bit_cast(h2, s.u[a]), s.e[a & 1], false);
+      pin(s.e[a & 1]);
     }
   }
   template <int I, int E>
@@ -1229,7 +1229,7 @@ struct Pipe {
     typename ES::State st;
     PolyState ps;
     PolyStateF psf;
-    psf.e = 0.f;
+    psf.e[0] = psf.e[1] = 0.f;
     GOp gn[2];
     f32x16 zn;
     if constexpr (HASG || !GRAD) {
@@ -1250,7 +1250,7 @@ struct Pipe {
         ES::all(zc, c, st);
     }
     if constexpr (POLY) {
-      if (FWD) e_acc += psf.e;
+      if (FWD) e_acc += psf.e[0] + psf.e[1];
       if (POS && __builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
       g[0] = gn[0];
       g[1] = gn[1];
@@ -1350,6 +1350,7 @@ struct RowsArgs {
   float2* rowpart; // [units][RW]
   int4* metpart;   // [units][RW]: Cut Metrics counts (predicted positive, true positive, positives)
   bool pos_apply;  // positives enter the tiles (c - 1, the loss's sum of their logits); false: counted only
+  uint8_t* rowform;  // [R_pad] (bf16, D <= 128): 1 where the row's waves took the polynomial epilogue, else 0
   float* topv;     // [units][RW][KT]: per-split top-KT logits (scoring)
   int32_t* topi;   // [units][RW][KT]: their item ids
 };
@@ -1438,6 +1439,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
     TopK<KT ? KT : 1> tk;
     if (KT) tk.init();
 
+    int poly_form = 0;  // epilogue the wave took (written per row for the finish)
     if constexpr (kPipe && kF16) {
       // |z| <= ||H[r]|| ||E[v]|| <= kPolyBoundF (kPolyBoundShort) for every logit of this wave: the polynomial
       // epilogue (its short form) applies
@@ -1454,6 +1456,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
       for (int o = 1; o < 32; o <<= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
       const float bound = sqrtf(n2) * __uint_as_float(a.ctl->enorm_max);
       const int form = __builtin_amdgcn_readfirstlane(bound <= kPolyBoundShort ? 2 : (bound <= kPolyBoundF ? 1 : 0));
+      poly_form = form;
       if (form == 2)
         pp.template run<2>((const bf16x8*)hop, acc, e_acc, posz);
       else if (form == 1)
@@ -1492,6 +1495,10 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
       const float e_tot = e_acc + __shfl_xor(e_acc, 32, 64);
       const float p_tot = posz + __shfl_xor(posz, 32, 64);
       if (lane < 32) a.rowpart[urow + lane] = make_float2(e_tot, p_tot);
+    }
+    if constexpr (std::is_same<T, __bf16>::value && evp_is_f16(1, D)) {
+      // every split of the row writes the same flag (the wave's choice depends on its rows and all of E only)
+      if (lane < 32) a.rowform[r_base + lane] = poly_form > 0 ? 1 : 0;
     }
     if (MET) {
 #pragma unroll
@@ -2295,6 +2302,7 @@ static RowsArgs rows_args(const Layout& L, char* ws, const void* E, bool pos_app
   a.n_vs = L.n_vs;
   a.R_pad = L.R_pad;
   a.dhpart = (float*)(ws + L.off_dhpart);
+  a.rowform = (uint8_t*)(ws + L.off_rowform);
   a.rowpart = (float2*)(ws + L.off_rowpart);
   a.metpart = (int4*)(ws + L.off_metpart);
   a.topv = (float*)(ws + L.off_dhpart);
