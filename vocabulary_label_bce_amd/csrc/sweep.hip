@@ -876,16 +876,21 @@ struct EpiPoly {
 // possible BCE term, softplus(-1) > 0.31) and 2.9e-6 on c. Short form (B = 0.45): loss through u^2, c through
 // u^2: errors below 3.2e-6 per loss term and 3.2e-6 on c, two operations less per pair of logits. The arithmetic
 // runs on packed f16 pairs (z rounded once to f16, relative 2^-11); the log cosh terms are summed in fp32 by
-// v_dot2_f32_f16 (exact f16 products) into two accumulators (even and odd pairs: two dependent chains of four
-// instead of one of eight), and c is written straight into the f16 G tile. The -z/2 terms are not summed here:
-// over a row's items they add up to the rank-1 -H[r].sum_v E[v] / 2, which the finish adds in float64 for the
-// rows flagged as polynomial (a third dot product per pair in the chain cost the sweep 5%).
+// v_dot2_f32_f16 (exact f16 products) into kPolyAcc accumulators carried over the unit's steps (pair a feeds
+// accumulator a % kPolyAcc: short dependent chains), and c is written straight into the f16 G tile. The -z/2
+// terms are not summed here: over a row's items they add up to the rank-1 -H[r].sum_v E[v] / 2, which the finish
+// adds in float64 for the rows flagged as polynomial. (Measured: a dot product per pair for -z/2 in one chain
+// with the rest cost the sweep 5%; two accumulators reset every step 0.6% against four carried ones.)
 // ---------------------------------------------------------------------------------------------------------
 constexpr float kPolyBoundF = 0.8f;       // long form
 constexpr float kPolyBoundShort = 0.45f;  // short form
+#ifndef CUTBCE_POLY_ACC
+#define CUTBCE_POLY_ACC 4
+#endif
+constexpr int kPolyAcc = CUTBCE_POLY_ACC;  // independent loss accumulators (pairs a, a + kPolyAcc, ... share one)
 struct PolyStateF {
   f16x2 zh[8], u[8], t[8], l[8];
-  float e[2];  // the step's log cosh terms, summed over the even and the odd pairs
+  float e[kPolyAcc];  // the sweep's log cosh terms so far, carried across steps
 };
 
 template <int NSLOT, bool SHORT>
@@ -958,8 +963,9 @@ struct EpiPolyF {
       s.l[a] = s.u[a] * (SHORT ? b2 : s.l[a]) + b1;
       pin(s.l[a]);
     } else if constexpr (kind == kLa) {  // + u (1/8 - u/192 + u^2/2880) for both logits
-      s.e[a & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.l[a]), __builtin_bit_cast(h2, s.u[a]), s.e[a & 1], false);
-      pin(s.e[a & 1]);
+      constexpr int q = a % kPolyAcc;
+      s.e[q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, s.l[a]), __builtin_bit_cast(h2, s.u[a]), s.e[q], false);
+      pin(s.e[q]);
     }
   }
   template <int I, int E>
@@ -1216,7 +1222,8 @@ struct Pipe {
   // POLY (F16G sweeps): the polynomial epilogue (EpiPoly in the dE sweep, EpiPolyF in the forward).
   template <bool HASG, int POLY>
   __device__ inline void iter(int i, int sAr, int sBr, int sAw, int sBw, bool bar, const bf16x8* own,
-                              f32x16* acc, f32x16& zc, float* c, GOp* g, float& e_acc, float& posz) {
+                              f32x16* acc, f32x16& zc, float* c, GOp* g, float& e_acc, float& posz,
+                              PolyStateF& psf) {
     static_assert(!POLY || (F16G && GRAD && !(FWD && POS)), "polynomial epilogue: f16 sweeps (forward: gathered positives)");
     static_assert(POLY != 2 || FWD, "short polynomial: forward only");
     const bool newblk = bar && (i & 63) == 0;
@@ -1228,8 +1235,6 @@ struct Pipe {
     if (newblk) bkt_dma((i >> 6) + 1);  // after the ring loads: the next barrier waits for nothing extra
     typename ES::State st;
     PolyState ps;
-    PolyStateF psf;
-    psf.e[0] = psf.e[1] = 0.f;
     GOp gn[2];
     f32x16 zn;
     if constexpr (HASG || !GRAD) {
@@ -1250,7 +1255,6 @@ struct Pipe {
         ES::all(zc, c, st);
     }
     if constexpr (POLY) {
-      if (FWD) e_acc += psf.e[0] + psf.e[1];
       if (POS && __builtin_expect((nem >> (i & 63)) & 1, 0)) positives_f16(i, gn);
       g[0] = gn[0];
       g[1] = gn[1];
@@ -1298,20 +1302,23 @@ struct Pipe {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float c[16];  // G tile of the last epilogue (exact epilogue)
     GOp g[2];     // the same, packed (polynomial epilogue)
+    PolyStateF psf;  // the forward polynomial's loss accumulators (carried over the unit's steps)
+#pragma unroll
+    for (int q = 0; q < kPolyAcc; ++q) psf.e[q] = 0.f;
     // iteration 0: logits of step 1, epilogue of step 0 (no gradient yet); with the barrier above it counts
     // as a barrier iteration (the one before the loop)
-    iter<false, POLY>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, g, e_acc, posz);
+    iter<false, POLY>(0, 1, 0, LA % NR, LB % NR, false, own, acc, zc, c, g, e_acc, posz, psf);
     int i = 1;
     // iterations 1 + 6m + u: slots A read (2 + u) % 6, B read u, A load u, B load (4 + u) % 6; barrier at odd u
     for (; i + NR - 1 < n; i += NR) {
 #pragma unroll
       for (int u = 0; u < NR; ++u)
         iter<true, POLY>(i + u, (2 + u) % NR, u, (1 + LA + u) % NR, (1 + LB + u) % NR, (u & 1) != 0, own, acc, zc, c,
-                         g, e_acc, posz);
+                         g, e_acc, posz, psf);
     }
     for (; i < n; ++i)
       iter<true, POLY>(i, (i + 1) % NR, (i - 1) % NR, (i + LA) % NR, (i + LB) % NR, (i & 1) == 0, own, acc, zc, c, g,
-                       e_acc, posz);
+                       e_acc, posz, psf);
     // iteration n: the gradient GEMM of step n - 1
     wait_vm_and_barrier<0>();
     if (GRAD) {
@@ -1319,6 +1326,12 @@ struct Pipe {
       const int s = (n - 1) % NR;
 #pragma unroll
       for (int m = 0; m < 2 * NDB; ++m) acc[m / 2] = mma_g(g[m % 2], rdB(s, m), acc[m / 2]);
+    }
+    if constexpr (POLY && FWD) {
+      float et = psf.e[0];
+#pragma unroll
+      for (int q = 1; q < kPolyAcc; ++q) et += psf.e[q];
+      e_acc += et;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
