@@ -1175,8 +1175,11 @@ struct Pipe {
   using ES = EpiOps<FWD, GRAD, NM, GOp>;
   static_assert(!GRAD || KS == 2 * NDB, "logit and gradient MFMAs alternate");
 
+  // gradient MFMA k of an iteration takes chunk gm(k): d-blocks in turn, first every d-block's first G half, then
+  // the second halves, so that MFMAs accumulating into one tile are NDB gradient MFMAs apart
+  static constexpr int gm(int k) { return (k % NDB) * 2 + k / NDB; }
   __device__ inline bf16x8 opnd_read(int j, int sAr, int sBr) const {
-    return GRAD ? ((j & 1) ? __builtin_bit_cast(bf16x8, rdB(sBr, j >> 1)) : rdA(sAr, j >> 1)) : rdA(sAr, j);
+    return GRAD ? ((j & 1) ? __builtin_bit_cast(bf16x8, rdB(sBr, gm(j >> 1))) : rdA(sAr, j >> 1)) : rdA(sAr, j);
   }
   // Slot J: MFMA J, its share of the epilogue, and the LDS read of the operand of MFMA J + RA. sched_barrier
   // keeps the slots in order (the compiler would otherwise issue each read right before its MFMA).
@@ -1189,7 +1192,8 @@ struct Pipe {
                                GOp* gn, bf16x8* opnd) const {
     if constexpr (J < NM) {
       if constexpr (GRAD && (J & 1))
-        acc[J >> 2] = mma_g((POLY ? g : st.g)[(J >> 1) & 1], __builtin_bit_cast(GOp, opnd[J]), acc[J >> 2]);
+        acc[gm(J >> 1) >> 1] = mma_g((POLY ? g : st.g)[gm(J >> 1) & 1], __builtin_bit_cast(GOp, opnd[J]),
+                                     acc[gm(J >> 1) >> 1]);
       else
         zn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[J], own[GRAD ? J >> 1 : J], zn, 0, 0, 0);
       if constexpr (POLY && FWD)
