@@ -258,6 +258,29 @@ def test_forward_f16_evp_scaling(e_scale, D):
     _check(p, _run(p, g=0.5), ref, excess=e_scale > 1e-3)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_evp_scale_follows_e_between_calls(D):
+    """The forward's f16 copy of E keeps the previous call's power-of-two scale while that scale still fits this
+    call's E, and is rewritten when it does not. One workspace, E rescaled between calls by 2^12, 2^-20 and back:
+    every call matches the oracle (the first call and each change of range take the rewrite)."""
+    p = W.custom_problem(300, 3000, D, dtype="bf16", seed=84, h_std=1.0 / math.sqrt(D), e_std=0.02,
+                         pos_per_row=(1, 6), mask_frac=0.1)
+    d = _dev(p)
+    w = Workspace(d["H"], d["E"], d["item_ids"], want_row_loss=True, save_dh=True)
+    gt = torch.tensor([1.0], device="cuda")
+    for k in (0, 12, 12, -20, 0, 0):
+        E = (p["E"].float() * 2.0 ** k).to(torch.bfloat16)
+        q = dict(p, E=E)
+        Ed = E.cuda()
+        w.forward(d["H"], Ed, d["row_offsets"], d["item_ids"], d["row_mask"])
+        dH, dE = w.backward(d["H"], Ed, d["row_offsets"], d["item_ids"], d["row_mask"], grad=gt, reuse=True)
+        torch.cuda.synchronize()
+        got = dict(loss=w.loss.item(), row_loss=w.row_loss.double().cpu().numpy(), dH=dH.double().cpu().numpy(),
+                   dE=dE.double().cpu().numpy())
+        ref = oracle.full(q["H"], q["E"], q["row_offsets"], q["item_ids"], q["row_mask"], g=1.0)
+        _check(q, got, ref, excess=k > -10)
+
+
 @pytest.mark.parametrize("h_scale,D", [(1e-5, 128), (3e3, 128), (1e-5, 512), (3e3, 256)])
 def test_de_f16_operand_scaling(h_scale, D):
     """The f16 copy of the rows used by the dE sweep is scaled by a power of two chosen from max |w H|: tiny and

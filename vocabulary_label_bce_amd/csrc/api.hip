@@ -84,7 +84,7 @@ Layout make_layout(const cutbce_problem* p) {
   L.off_metpart = take(sizeof(int32_t) * 4 * (size_t)part_rows);
   L.off_rowloss = take(sizeof(double) * L.R_pad);
   L.off_dhtmp = take(sizeof(float) * (size_t)L.R * L.D);
-  L.off_estat = take(sizeof(float) * 2 * 2048);  // E statistics: two maxima per block (at most 2,048 blocks)
+  L.off_estat = take(sizeof(float) * 2 * (size_t)L.n_eblk);  // E statistics: two maxima per preparation block
   L.off_rowform = take((size_t)L.R_pad);
   L.off_bptr_r = take(sizeof(int32_t) * (L.nb_r + 1));
   L.off_bfill_r = take(sizeof(int32_t) * L.nb_r);

@@ -74,8 +74,10 @@ struct Ctl {           // device control block
   double scale;        // s = 1 / (W * V), W = summed weight of the valid rows (R_v without weights); 0 when W == 0
   uint32_t hnorm_max;  // bits of max_r ||H[r]|| over the valid rows (a non-negative float), set by the H preparation
   uint32_t hw_absmax;  // bits of max |w_r H[r][d]| over the valid rows (the f16 gradient operand's scale)
-  uint32_t enorm_max;  // bits of max_v ||E[v]|| (set by the E statistics pass of the f16-Evp shapes)
-  uint32_t e_absmax;   // bits of max |E[v][d]| (the f16 slot-packed E copy's scale; same pass)
+  uint32_t enorm_max;  // bits of max_v ||E[v]|| (from the E preparation's statistics, f16-Evp shapes)
+  uint32_t e_absmax;   // bits of max |E[v][d]| (same)
+  int32_t evp_shift;   // the power of two the f16 Evp holds E scaled by; kept from call to call (not reset)
+  int32_t evp_fix;     // 1 when this call's E needs another scale than the previous call's: Evp is rewritten
 };
 
 // Shapes whose dE sweep runs its gradient GEMM in f16 (every bf16 input): the slot-packed rows Hrp are stored as
@@ -90,9 +92,11 @@ __host__ __device__ constexpr inline bool hrp_is_f16(int dtype, int D) { return 
 __host__ __device__ constexpr inline bool narrow_owner(int dtype, int D) { return dtype == 1 && D >= 256; }
 
 // Shapes whose forward sweep runs its gradient GEMM in f16 (bf16 input on the 32-owner engines, D <= 128): the
-// slot-packed E copy Evp is stored as f16 scaled by 2^hrp_shift(e_absmax), the G tiles are f16, and the dH
-// partials are multiplied by 2^-shift when written. The E statistics pass (max ||E[v]||, max |E|) runs first;
-// the row norm bound also lets the forward sweep take its polynomial epilogue.
+// slot-packed E copy Evp is stored as f16 scaled by 2^evp_shift, the G tiles are f16, and the dH partials are
+// multiplied by 2^-evp_shift when written. The E preparation writes Evp with the previous call's shift and takes
+// max ||E[v]|| and max |E| on the way; the shift stands if it puts max |E| in [2^13, 2^15), else a second pass
+// rewrites Evp with the shift that puts it in [2^14, 2^15). The norm bound also lets the forward sweep take its
+// polynomial epilogue.
 __host__ __device__ constexpr inline bool evp_is_f16(int dtype, int D) { return dtype == 1 && D <= 128; }
 __host__ __device__ constexpr inline int sp16_row(int lane, int j) { return 16 * (j / 4) + 4 * (lane / 16) + (j % 4); }
 __host__ __device__ constexpr inline int64_t sp16_off(int db, int lane) { return ((int64_t)db * 64 + lane) * 8; }
@@ -108,6 +112,12 @@ __device__ inline int hrp_shift(uint32_t absmax_bits) {
   return k < -120 ? -120 : (k > 120 ? 120 : k);
 }
 
+// The shift an f16 Evp was written with (clamped, so that a workspace that never held one gives a finite scale).
+__device__ inline int evp_shift_of(const Ctl* ctl) {
+  const int k = ctl->evp_shift;
+  return k < -120 ? -120 : (k > 120 ? 120 : k);
+}
+
 struct Layout {
   int64_t R, V, nnz;
   int D, dtype, esz;
@@ -120,7 +130,7 @@ struct Layout {
   int64_t nb_r, nb_i; // bucket counts (forward: row tile x item step; backward: item tile x row step)
   size_t off_ctl, off_row_of, off_compact_of, off_rptr, off_wc, off_Hc, off_Hrp, off_sumH, off_sumH_part;
   size_t off_sumE, off_sumE_part, off_sum2, off_Evp, off_dhpart, off_rowpart, off_metpart, off_rowloss, off_dhtmp;
-  size_t off_estat;  // per-block maxima of the E statistics pass
+  size_t off_estat;  // per-block maxima of the E statistics (two floats per E preparation block)
   size_t off_rowform;  // per compacted row: 1 if the forward's waves took the polynomial epilogue (bf16, D <= 128)
   size_t off_bptr_r, off_bfill_r, off_pairs_r, off_bptr_i, off_bfill_i, off_pairs_i, off_scan, off_cpart;
   size_t scan_elems;

@@ -439,67 +439,19 @@ hipError_t launch_prep_hrp(const Layout& L, char* ws, const void* H, hipStream_t
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------------------------------
-// E statistics (bf16, D <= 128): max_v ||E[v]|| and max |E[v][d]|. One item per group of D/8 lanes, one 16-byte
-// load per lane, grid-stride over the items; each block writes its two maxima to part[2 b], part[2 b + 1], and
-// k_stats_e_final folds them into the control block (no contended atomics: one per block on a single address
-// measured about 80 us at 2,048 blocks). NaNs do not enter the maxima (fmaxf); a NaN in E gives NaN logits, and
-// so NaN outputs, on either forward epilogue.
-// ---------------------------------------------------------------------------------------------------------
-constexpr int kStatBlocks = 2048;  // most blocks of the E statistics pass
-
-template <int D>
-__global__ void __launch_bounds__(256) k_stats_e(const __bf16* __restrict__ E, int64_t V, float* __restrict__ part) {
-  constexpr int LPI = D / 8;          // lanes per item
-  constexpr int IPB = 256 / LPI;      // items per block and pass
-  __shared__ float sh_n[4], sh_a[4];
-  constexpr int U = 4;                // items per lane group and pass, loaded before any is reduced
-  const int tid = threadIdx.x, sub = tid % LPI;
-  const int64_t stride = (int64_t)gridDim.x * IPB;
-  float nmax = 0.f, amax = 0.f;
-  for (int64_t v0 = (int64_t)blockIdx.x * IPB; v0 < V; v0 += U * stride) {  // block-uniform trip count
-    bf16x8 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t v = v0 + u * stride + tid / LPI;
-      x[u] = v < V ? *(const bf16x8*)(E + v * D + sub * 8) : bf16x8{};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float n2 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float f = (float)x[u][j];
-        n2 += f * f;
-        amax = fmaxf(amax, __builtin_fabsf(f));
-      }
-#pragma unroll
-      for (int o = 1; o < LPI; o <<= 1) n2 += __shfl_xor(n2, o, 64);
-      nmax = fmaxf(nmax, n2);
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    nmax = fmaxf(nmax, __shfl_xor(nmax, o, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  }
-  if (tid % 64 == 0) {
-    sh_n[tid / 64] = nmax;
-    sh_a[tid / 64] = amax;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    part[2 * blockIdx.x] = sqrtf(fmaxf(fmaxf(sh_n[0], sh_n[1]), fmaxf(sh_n[2], sh_n[3])));
-    part[2 * blockIdx.x + 1] = fmaxf(fmaxf(sh_a[0], sh_a[1]), fmaxf(sh_a[2], sh_a[3]));
-  }
-}
-
-// One block: the largest of the blocks' maxima.
-__global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict__ part, int nblk, Ctl* __restrict__ ctl) {
+// E statistics of the f16-Evp shapes (bf16, D <= 128): one block folds the E preparation blocks' maxima
+// (max ||E[v]||, max |E|; NaNs do not enter them, and a NaN in E gives NaN outputs on either forward epilogue)
+// into the control block, and decides whether the shift Evp was written with stands: it must put max |E| in
+// [2^13, 2^15) (no f16 overflow; 11 significant bits for every value within 2^27 of the largest). Otherwise it
+// records the shift that puts max |E| in [2^14, 2^15) and sets evp_fix, and the fix-up pass of k_prep_e rewrites
+// Evp. (Scaling from statistics of a separate pass over E before the preparation cost one more read of E,
+// 45 us at 876,000 x 128.)
+__global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict__ part, int64_t nblk,
+                                                        Ctl* __restrict__ ctl) {
   __shared__ float sh[2][16];
   const int tid = threadIdx.x;
   float n = 0.f, a = 0.f;
-  for (int b = tid; b < nblk; b += 1024) {
+  for (int64_t b = tid; b < nblk; b += 1024) {
     n = fmaxf(n, part[2 * b]);
     a = fmaxf(a, part[2 * b + 1]);
   }
@@ -520,20 +472,30 @@ __global__ void __launch_bounds__(1024) k_stats_e_final(const float* __restrict_
     }
     ctl->enorm_max = __float_as_uint(n);
     ctl->e_absmax = __float_as_uint(a);
+    const int used = evp_shift_of(ctl), want = hrp_shift(__float_as_uint(a));
+    const bool fix = !(used == want || used == want - 1);
+    ctl->evp_fix = fix ? 1 : 0;
+    if (fix) ctl->evp_shift = want;
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
 // E preparation: block = kEBlkItems items, processed 32 at a time through LDS. Writes the slot-packed Evp
-// (when requested; f16 scaled by 2^hrp_shift(e_absmax) for the evp_is_f16 shapes) and float64 column sums per
-// block.
+// (when requested; f16 scaled by 2^evp_shift for the evp_is_f16 shapes) and float64 column sums per block; for
+// the f16-Evp shapes also the block's max ||E[v]|| and max |E| (stat[2 b], stat[2 b + 1]). FIX: the fix-up pass
+// (launched after k_stats_e_final): every block returns at once unless evp_fix is set, and then only rewrites
+// Evp with the new shift.
 // ---------------------------------------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool FIX = false>
 __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t V, T* __restrict__ Evp,
-                                                double* __restrict__ sum_part, const Ctl* __restrict__ ctl) {
+                                                double* __restrict__ sum_part, const Ctl* __restrict__ ctl,
+                                                float* __restrict__ stat) {
   extern __shared__ char smem_raw[];
   T* tile = (T*)smem_raw;  // [32][D]
   const int tid = threadIdx.x;
+  if (FIX && ctl->evp_fix == 0) return;  // block-uniform
+  constexpr bool kStats = sizeof(T) == 2 && evp_is_f16(1, D) && !FIX;
+  float nmax = 0.f, amax = 0.f;  // kStats: this thread's largest item norm^2 and |value| so far
   constexpr int upr = D * (int)sizeof(T) / 16;  // 16-byte units per row
   constexpr int kU = 32 * upr / 256;             // units per thread and 32-item chunk (1 ... 8)
   static_assert(kU >= 1 && 32 * upr % 256 == 0, "whole units per thread");
@@ -574,10 +536,26 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
         packed = true;
       }
     }
+    if constexpr (kStats) {
+      if (stat) {
+        // 8 threads per item of the chunk (padding items are zero)
+        const int it = tid / 8, sub = tid % 8;
+        float n2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < D / 8; ++k) {
+          const float x = (float)tile[it * D + sub + 8 * k];
+          n2 += x * x;
+          amax = fmaxf(amax, __builtin_fabsf(x));
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) n2 += __shfl_xor(n2, o, 64);
+        nmax = fmaxf(nmax, n2);
+      }
+    }
     if constexpr (sizeof(T) == 2 && evp_is_f16(1, D)) {
       if (Evp) {
         _Float16* dst = (_Float16*)(Evp + v0 * D);
-        const float sc = ldexpf(1.f, hrp_shift(ctl->e_absmax));
+        const float sc = ldexpf(1.f, evp_shift_of(ctl));
         for (int q = tid; q < (D / 32) * 2 * 64; q += 256) {
           const int lane = q % 64, g = (q / 64) % 2, db = q / 128;
           f16x8 run;
@@ -598,31 +576,51 @@ __global__ void __launch_bounds__(256) k_prep_e(const T* __restrict__ E, int64_t
         *(typename Elem<T>::Op*)(dst + o) = run;
       }
     }
-    if (tid < D)
-      for (int rr = 0; rr < 32; ++rr) acc0 += (double)(float)tile[rr * D + tid];
-    if (tid + 256 < D)
-      for (int rr = 0; rr < 32; ++rr) acc1 += (double)(float)tile[rr * D + tid + 256];
+    if (!FIX) {
+      if (tid < D)
+        for (int rr = 0; rr < 32; ++rr) acc0 += (double)(float)tile[rr * D + tid];
+      if (tid + 256 < D)
+        for (int rr = 0; rr < 32; ++rr) acc1 += (double)(float)tile[rr * D + tid + 256];
+    }
     __syncthreads();
   }
+  if (FIX) return;
   if (tid < D) sum_part[blockIdx.x * (int64_t)D + tid] = acc0;
   if (tid + 256 < D) sum_part[blockIdx.x * (int64_t)D + tid + 256] = acc1;
+  if constexpr (kStats) {
+    if (stat) {
+      __shared__ float sh_n[4], sh_a[4];
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, o, 64));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      if (tid % 64 == 0) {
+        sh_n[tid / 64] = nmax;
+        sh_a[tid / 64] = amax;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        stat[2 * blockIdx.x] = sqrtf(fmaxf(fmaxf(sh_n[0], sh_n[1]), fmaxf(sh_n[2], sh_n[3])));
+        stat[2 * blockIdx.x + 1] = fmaxf(fmaxf(sh_a[0], sh_a[1]), fmaxf(sh_a[2], sh_a[3]));
+      }
+    }
+  }
 }
 
 template <typename T, int D>
 static void prep_e_launch(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {
   Ctl* ctl = (Ctl*)(ws + L.off_ctl);
-  if constexpr (sizeof(T) == 2 && evp_is_f16(1, D)) {
-    if (want_evp) {
-      const int64_t need = (L.V + 256 / (D / 8) - 1) / (256 / (D / 8));
-      const int blocks = (int)(need < kStatBlocks ? need : kStatBlocks);
-      float* part = (float*)(ws + L.off_estat);
-      hipLaunchKernelGGL((k_stats_e<D>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)E, L.V, part);
-      hipLaunchKernelGGL(k_stats_e_final, dim3(1), dim3(1024), 0, st, (const float*)part, blocks, ctl);
-    }
+  constexpr bool kF16 = sizeof(T) == 2 && evp_is_f16(1, D);
+  float* stat = kF16 && want_evp ? (float*)(ws + L.off_estat) : nullptr;
+  T* evp = want_evp ? (T*)(ws + L.off_Evp) : nullptr;
+  const size_t sm = (size_t)32 * D * sizeof(T);
+  hipLaunchKernelGGL((k_prep_e<T, D>), dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const T*)E, L.V, evp,
+                     (double*)(ws + L.off_sumE_part), (const Ctl*)ctl, stat);
+  if (stat) {
+    hipLaunchKernelGGL(k_stats_e_final, dim3(1), dim3(1024), 0, st, (const float*)stat, L.n_eblk, ctl);
+    hipLaunchKernelGGL((k_prep_e<T, D, true>), dim3((unsigned)L.n_eblk), dim3(256), sm, st, (const T*)E, L.V, evp,
+                       (double*)nullptr, (const Ctl*)ctl, (float*)nullptr);
   }
-  hipLaunchKernelGGL((k_prep_e<T, D>), dim3((unsigned)L.n_eblk), dim3(256), (size_t)32 * D * sizeof(T), st,
-                     (const T*)E, L.V, want_evp ? (T*)(ws + L.off_Evp) : nullptr, (double*)(ws + L.off_sumE_part),
-                     (const Ctl*)ctl);
 }
 
 hipError_t launch_prep_e(const Layout& L, char* ws, const void* E, bool want_evp, hipStream_t st) {

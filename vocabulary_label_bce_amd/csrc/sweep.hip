@@ -1524,7 +1524,7 @@ __global__ void __launch_bounds__(NW * 64) k_rows(RowsArgs a) {
       if (lane < 32) a.metpart[urow + lane] = make_int4(met[0], met[1], met[2], 0);
     }
     if (WITH_DH) {
-      const float unscale = kF16 ? ldexpf(1.f, -hrp_shift(a.ctl->e_absmax)) : 1.f;
+      const float unscale = kF16 ? ldexpf(1.f, -evp_shift_of(a.ctl)) : 1.f;
 #pragma unroll
       for (int db = 0; db < NDBE; ++db)
 #pragma unroll
