@@ -184,8 +184,8 @@ def mfma_ceiling(torch, B, dev):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": f"bench.py measures one GPU only (--gpus {a.gpus} requested); the path has no "
-                                   "multi-GPU mode in this build"}))
+        print(json.dumps({"error": f"bench.py measures one GPU only (--gpus {a.gpus} requested): the library "
+                                   "drives one GPU per process and has no multi-GPU mode"}))
         sys.exit(2)
     import torch
 
