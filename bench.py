@@ -158,25 +158,30 @@ def bench_topk(a, cfg, prob, R_v):
     }))
 
 
-def mfma_ceiling(torch, B, dev):
+def mfma_ceiling(torch, B, dev, random_operands=False):
     """MFMA-only ceiling (cutbce_mfma_ceiling): one workgroup of 8 waves per CU (two per SIMD, as in the D = 128
     sweeps), each issuing v_mfma_f32_32x32x16_bf16 back to back from registers. Returns its rate and the shader
-    clock the device held meanwhile (s_memtime over s_memrealtime ticks, median over waves)."""
+    clock the device held meanwhile (s_memtime over s_memrealtime ticks, median over waves). With
+    random_operands (cutbce_mfma_ceiling_random) the operands are random and change from one MFMA to the next,
+    as the sweeps' tiles do, so the clock includes data-dependent power."""
+    run = B.mfma_ceiling_random if random_operands else B.mfma_ceiling
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     waves, iters = 8, 50000
     stamps = torch.zeros(4 * blocks * waves, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    B.mfma_ceiling(blocks, waves, iters, stamps, stream)  # warm-up launch
+    run(blocks, waves, iters, stamps, stream)  # warm-up launch
     ev0.record(stream)
-    B.mfma_ceiling(blocks, waves, iters, stamps, stream)
+    run(blocks, waves, iters, stamps, stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
     st = stamps.view(-1, 4).double()
     ghz = (0.1 * (st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).median().item()
     tflops = blocks * waves * iters * 4 * 32768 / (ms * 1e-3) / 1e12
-    return {"kernel": "k_mfma_ceiling (v_mfma_f32_32x32x16_bf16 from registers, 8 waves per CU)",
+    name = "k_mfma_ceiling_random (random operands changing every MFMA" if random_operands else \
+        "k_mfma_ceiling (constant operands"
+    return {"kernel": name + "; v_mfma_f32_32x32x16_bf16 from registers, 8 waves per CU)",
             "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "clock_ghz": round(ghz, 3), "ms": round(ms, 3), "iters": iters, "blocks": blocks, "waves": waves}
 
@@ -279,10 +284,11 @@ def main():
         "loss": loss0,
         "memory": memory,
     }
-    ceil = mfma_ceiling(torch, B, dev)
-    if dom:
-        ceil["dominant_kernel_frac_of_ceiling"] = round(kern[dom]["tflops"] / ceil["tflops"], 4)
-    out["mfma_ceiling"] = ceil
+    for key, rnd in (("mfma_ceiling", False), ("mfma_ceiling_random", True)):
+        ceil = mfma_ceiling(torch, B, dev, random_operands=rnd)
+        if dom:
+            ceil["dominant_kernel_frac_of_ceiling"] = round(kern[dom]["tflops"] / ceil["tflops"], 4)
+        out[key] = ceil
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prob, R_v, a.cpu_seconds)
     if a.copy_mib > 0:

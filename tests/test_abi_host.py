@@ -198,6 +198,11 @@ def test_mfma_ceiling_rejects_bad_arguments():
     assert L.cutbce_mfma_ceiling(1, 8, 0, 8, None) == 2        # no iterations
     assert L.cutbce_mfma_ceiling(1, 8, 10, None, None) == 1    # no stamp buffer
     assert L.cutbce_mfma_ceiling(1, 8, 10, 12, None) == 4      # misaligned stamp buffer
+    assert L.cutbce_mfma_ceiling_random(0, 8, 10, 8, None) == 2
+    assert L.cutbce_mfma_ceiling_random(1, 17, 10, 8, None) == 2
+    assert L.cutbce_mfma_ceiling_random(1, 8, 0, 8, None) == 2
+    assert L.cutbce_mfma_ceiling_random(1, 8, 10, None, None) == 1
+    assert L.cutbce_mfma_ceiling_random(1, 8, 10, 12, None) == 4
 
 
 def test_noalloc_forward_rejects_problems_beyond_its_scratch_before_any_hip_call():

@@ -1,4 +1,5 @@
-"""The MFMA-only ceiling kernel (cutbce_mfma_ceiling) that bench.py reports beside the sweeps: it runs, every
+"""The MFMA-only ceiling kernels (cutbce_mfma_ceiling on constant operands, cutbce_mfma_ceiling_random on
+random operands that change every MFMA) that bench.py reports beside the sweeps: each runs, every
 wave records increasing timestamps, and the rate and clock it implies are physically possible (at most the
 published dense bf16 peak at the 2.4 GHz peak clock)."""
 import pytest
@@ -9,14 +10,15 @@ from vocabulary_label_bce_amd import binding as B
 pytestmark = pytest.mark.gpu
 
 
-def test_mfma_ceiling_stamps_and_rate():
+@pytest.mark.parametrize("run", [B.mfma_ceiling, B.mfma_ceiling_random], ids=["constant", "random"])
+def test_mfma_ceiling_stamps_and_rate(run):
     blocks, waves, iters = 64, 8, 2000
     stamps = torch.zeros(4 * blocks * waves, dtype=torch.int64, device="cuda")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s = torch.cuda.current_stream()
-    B.mfma_ceiling(blocks, waves, iters, stamps, s)
+    run(blocks, waves, iters, stamps, s)
     ev0.record(s)
-    B.mfma_ceiling(blocks, waves, iters, stamps, s)
+    run(blocks, waves, iters, stamps, s)
     ev1.record(s)
     torch.cuda.synchronize()
     st = stamps.view(-1, 4).cpu()

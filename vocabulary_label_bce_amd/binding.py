@@ -33,7 +33,8 @@ class Problem(ctypes.Structure):
 EXPORTS = ["cutbce_workspace_size", "cutbce_forward", "cutbce_forward_noalloc", "cutbce_backward",
            "cutbce_backward_reuse", "cutbce_validate_targets",
            "cutbce_targets_to_csr", "cutbce_topk",
-           "cutbce_profile_enable", "cutbce_profile_read", "cutbce_mfma_ceiling", "cutbce_status_string",
+           "cutbce_profile_enable", "cutbce_profile_read", "cutbce_mfma_ceiling",
+           "cutbce_mfma_ceiling_random", "cutbce_status_string",
            "cutbce_version"]
 
 
@@ -62,6 +63,8 @@ def lib():
         L.cutbce_profile_read.restype = i32
         L.cutbce_mfma_ceiling.argtypes = [i32, i32, i32, vp, vp]
         L.cutbce_mfma_ceiling.restype = i32
+        L.cutbce_mfma_ceiling_random.argtypes = [i32, i32, i32, vp, vp]
+        L.cutbce_mfma_ceiling_random.restype = i32
         L.cutbce_status_string.argtypes = [i32]
         L.cutbce_status_string.restype = ctypes.c_char_p
         L.cutbce_version.restype = i32
@@ -178,3 +181,8 @@ def profile_read() -> dict:
 def mfma_ceiling(blocks: int, waves_per_block: int, iters: int, stamps, stream=None):
     """Enqueue the MFMA-only ceiling kernel; stamps: int64 device tensor of 4 * blocks * waves_per_block."""
     _check(lib().cutbce_mfma_ceiling(blocks, waves_per_block, iters, _ptr(stamps), _stream(stream)))
+
+
+def mfma_ceiling_random(blocks: int, waves_per_block: int, iters: int, stamps, stream=None):
+    """Enqueue the MFMA-only ceiling kernel on random operands that change from one MFMA to the next."""
+    _check(lib().cutbce_mfma_ceiling_random(blocks, waves_per_block, iters, _ptr(stamps), _stream(stream)))
