@@ -162,8 +162,8 @@ def mfma_ceiling(torch, B, dev, random_operands=False):
     """MFMA-only ceiling (cutbce_mfma_ceiling): one workgroup of 8 waves per CU (two per SIMD, as in the D = 128
     sweeps), each issuing v_mfma_f32_32x32x16_bf16 back to back from registers. Returns its rate and the shader
     clock the device held meanwhile (s_memtime over s_memrealtime ticks, median over waves). With
-    random_operands (cutbce_mfma_ceiling_random) the operands are random and change from one MFMA to the next,
-    as the sweeps' tiles do, so the clock includes data-dependent power."""
+    random_operands (cutbce_mfma_ceiling_random) the operands are random bf16 values, as the sweeps' tiles are,
+    so the clock includes the multipliers' data-dependent power."""
     run = B.mfma_ceiling_random if random_operands else B.mfma_ceiling
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     waves, iters = 8, 50000
@@ -179,7 +179,7 @@ def mfma_ceiling(torch, B, dev, random_operands=False):
     st = stamps.view(-1, 4).double()
     ghz = (0.1 * (st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2])).median().item()
     tflops = blocks * waves * iters * 4 * 32768 / (ms * 1e-3) / 1e12
-    name = "k_mfma_ceiling_random (random operands changing every MFMA" if random_operands else \
+    name = "k_mfma_ceiling_random (random operands" if random_operands else \
         "k_mfma_ceiling (constant operands"
     return {"kernel": name + "; v_mfma_f32_32x32x16_bf16 from registers, 8 waves per CU)",
             "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),

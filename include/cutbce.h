@@ -206,10 +206,10 @@ cutbce_status cutbce_profile_read(double *ms, int64_t *launches, int n_kinds);
  * Errors: SHAPE for counts out of range, NULL, ALIGN. Asynchronous on `stream`. */
 cutbce_status cutbce_mfma_ceiling(int blocks, int waves_per_block, int iters, long long *stamps, void *stream);
 
-/* The same ceiling on operands that change from one MFMA to the next (a measurement, not part of the loss): each
- * wave holds four register sets of random bf16 values in [-1, 1), one per accumulator tile, so every MFMA
- * switches about half of its input bits as the sweeps' operand tiles do; the clock it holds includes that
- * data-dependent power. Arguments, stamps, flops per round and errors as for cutbce_mfma_ceiling. */
+/* The same ceiling on random operands (a measurement, not part of the loss): each wave holds four register sets
+ * of random bf16 values in [-1, 1), one per accumulator tile, like the sweeps' operand tiles; the multipliers'
+ * power on such values lowers the clock the device holds. Arguments, stamps, flops per round and errors as for
+ * cutbce_mfma_ceiling. */
 cutbce_status cutbce_mfma_ceiling_random(int blocks, int waves_per_block, int iters, long long *stamps,
                                          void *stream);
 

@@ -1,5 +1,5 @@
 """The MFMA-only ceiling kernels (cutbce_mfma_ceiling on constant operands, cutbce_mfma_ceiling_random on
-random operands that change every MFMA) that bench.py reports beside the sweeps: each runs, every
+random operands) that bench.py reports beside the sweeps: each runs, every
 wave records increasing timestamps, and the rate and clock it implies are physically possible (at most the
 published dense bf16 peak at the 2.4 GHz peak clock)."""
 import pytest

@@ -51,10 +51,11 @@ __device__ inline uint32_t fmix32(uint32_t h) {
   return h;
 }
 
-// The same loop on operands that change from one MFMA to the next: four register sets of random bf16 values,
-// uniform in [-1, 1) with random mantissas, one set per accumulator tile. The constant operands of
-// k_mfma_ceiling barely switch the multipliers' inputs; here each MFMA switches about half of its input bits, as
-// the sweeps' operand tiles do, so the clock the device holds reflects data-dependent power.
+// The same loop on random operands: four register sets of bf16 values uniform in [-1, 1) with random mantissas,
+// one set per accumulator tile, as the sweeps' operand tiles hold. The multipliers draw more power on such values
+// than on the near-constant ones of k_mfma_ceiling (the power follows the values inside each MFMA: one fixed
+// random set gives the same rate as sets that change every MFMA), so the clock the device holds here is the one
+// data like the sweeps' allows.
 __global__ void __launch_bounds__(1024) k_mfma_ceiling_random(int iters, long long* __restrict__ stamps) {
   const int lane = lane_of();
   const uint32_t w = (uint32_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
